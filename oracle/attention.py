@@ -1,0 +1,166 @@
+"""Oracle: dense masked softmax attention and its analytic backward, float64.
+
+Test infrastructure only.  The definition followed (CompileMask paper summary,
+section 3.3.2 "Descriptor-Guided Attention Execution"): scores of invisible
+(query, key) pairs are replaced by minus infinity before the softmax; the
+result is the ordinary softmax attention over the visible keys.
+
+Readings where the pages are silent:
+  * scale = 1 / sqrt(d);
+  * lse is the natural-log log-sum-exp of the scaled visible scores;
+  * a query row with no visible key has O = 0 and lse = -inf, its dQ row is 0
+    and it adds nothing to dK or dV;
+  * the backward uses D = rowsum(dO * O) with the oracle's own float64 O.
+
+Inputs are numpy or torch arrays [B, H, N, d] (bf16 values are upcast exactly).
+``mask_rows(b, r0, r1)`` returns the boolean visibility of rows r0..r1-1
+against every key of sample b.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, np.float64)
+
+
+def _scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward_head(q, k, v, mask_rows, b: int, rows=None, scale=None, block: int = 1024):
+    """Forward of one (b, h) pair.  q, k, v are float64 [N, d].
+
+    Returns O [len(rows), d] and lse [len(rows)] for the given rows (all rows
+    by default).
+    """
+    N, d = q.shape
+    sc = _scale(d, scale)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    O = np.zeros((len(rows), d))
+    lse = np.full(len(rows), -np.inf)
+    for a in range(0, len(rows), block):
+        rr = rows[a: a + block]
+        M = _rows_mask(mask_rows, b, rr)
+        S = (q[rr] @ k.T) * sc
+        S[~M] = -np.inf
+        m = S.max(axis=1)
+        live = np.isfinite(m)
+        P = np.zeros_like(S)
+        P[live] = np.exp(S[live] - m[live, None])
+        l = P.sum(axis=1)
+        O[a: a + len(rr)][live] = (P[live] @ v) / l[live, None]
+        lse[a: a + len(rr)][live] = m[live] + np.log(l[live])
+    return O, lse
+
+
+def _rows_mask(mask_rows, b, rr):
+    rr = np.asarray(rr)
+    if len(rr) and np.all(np.diff(rr) == 1):
+        return mask_rows(b, int(rr[0]), int(rr[-1]) + 1)
+    return np.vstack([mask_rows(b, int(r), int(r) + 1) for r in rr])
+
+
+def probabilities(q, k, lse, M, scale=None):
+    """P = exp(S - lse) on visible pairs, 0 elsewhere and on empty rows."""
+    d = q.shape[-1]
+    S = (q @ k.T) * _scale(d, scale)
+    P = np.zeros_like(S)
+    live = np.isfinite(lse)
+    Sl = S[live]
+    Pl = np.exp(Sl - lse[live, None])
+    Pl[~M[live]] = 0.0
+    P[live] = Pl
+    return P
+
+
+def backward_head(q, k, v, do, mask_rows, b: int, scale=None, block: int = 1024):
+    """Analytic backward of one (b, h) pair; float64 [N, d] inputs.
+
+    Returns dq, dk, dv (float64 [N, d]) and the forward O, lse it used.
+    """
+    N, d = q.shape
+    sc = _scale(d, scale)
+    O, lse = forward_head(q, k, v, mask_rows, b, scale=scale, block=block)
+    Dvec = np.sum(do * O, axis=1)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        M = mask_rows(b, r0, r1)
+        P = probabilities(q[r0:r1], k, lse[r0:r1], M, scale)
+        dv += P.T @ do[r0:r1]
+        dP = do[r0:r1] @ v.T
+        dS = P * (dP - Dvec[r0:r1, None])
+        dq[r0:r1] = (dS @ k) * sc
+        dk += (dS.T @ q[r0:r1]) * sc
+    return dq, dk, dv, O, lse
+
+
+def forward(q, k, v, mask_rows, scale=None, block: int = 1024):
+    """All heads: O [B,H,N,d], lse [B,H,N] (float64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], mask_rows, b, scale=scale, block=block)
+    return O, lse
+
+
+def backward(q, k, v, do, mask_rows, scale=None, block: int = 1024):
+    """All heads: dq, dk, dv [B,H,N,d] (float64), plus O and lse."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    O = np.zeros_like(q)
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h], O[b, h], lse[b, h] = backward_head(
+                q[b, h], k[b, h], v[b, h], do[b, h], mask_rows, b, scale=scale, block=block)
+    return dq, dk, dv, O, lse
+
+
+def sampled_head(q, k, v, do, mask_rows, b: int, rows, keys, scale=None, block: int = 1024):
+    """Full-size spot check of one (b, h) pair.
+
+    Runs the whole forward (every row's lse and O are needed by the backward),
+    then returns O, lse, dq at ``rows`` and dk, dv at ``keys``.
+    """
+    N, d = q.shape
+    sc = _scale(d, scale)
+    O, lse = forward_head(q, k, v, mask_rows, b, scale=scale, block=block)
+    Dvec = np.sum(do * O, axis=1)
+    rows = np.asarray(rows)
+    keys = np.asarray(keys)
+    # dq at the sampled rows
+    M = _rows_mask(mask_rows, b, rows)
+    P = probabilities(q[rows], k, lse[rows], M, scale)
+    dS = P * (do[rows] @ v.T - Dvec[rows, None])
+    dq = (dS @ k) * sc
+    # dk, dv at the sampled keys: sum over every row block
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        Mk = mask_rows(b, r0, r1)[:, keys]
+        Pk = probabilities(q[r0:r1], k[keys], lse[r0:r1], Mk, scale)
+        dv += Pk.T @ do[r0:r1]
+        dSk = Pk * (do[r0:r1] @ v[keys].T - Dvec[r0:r1, None])
+        dk += (dSk.T @ q[r0:r1]) * sc
+    return dict(O=O[rows], lse=lse[rows], dq=dq, dk=dk, dv=dv, visible_rows=M.sum(axis=1))
