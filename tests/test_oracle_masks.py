@@ -271,6 +271,13 @@ def test_flashmask_two_interval_limit():
     # a row of segment 7 (refs {5}) merges to three runs
     row = od.runs_of_rows(M[60:61])[0]
     assert row == [(0, 4), (44, 52), (60, 61)]
+    # largest run count per 16-wide tile, counted by hand from the segment
+    # table above (columns: own segment tail plus every referencing segment;
+    # rows: prefix, own segment head and referenced segments, merged)
+    tiles = (16, 16, 16, 16)
+    v = od.View(od.build("retrieval", md, 4, 4, tiles), 1, 68, 4, 4, tiles)
+    assert v["col_tkmax"][0].tolist() == [4, 2, 2, 2, 1]
+    assert v["row_tkmax"][0].tolist() == [2, 3, 3, 3, 3]
 
 
 def test_metadata_validation_bits_and_empty_sample():
