@@ -1,0 +1,225 @@
+/*
+ * compilemask.h -- C ABI of the MI355X (gfx950) CompileMask hot path.
+ *
+ * What the library computes (CompileMask paper summary):
+ *   - a MaskSpec groups query rows into Regions, each with a row guard and a
+ *     visibility rule (section 3.2 "Offline Mask Specification and
+ *     Compilation", section 3.2.1 "Mask Specification");
+ *   - the spec is lowered once, offline, to visible-interval endpoints; the
+ *     number of interval slots is derived per Region from its rule (section
+ *     3.2.2 "Symbolic Lowering to Visible Intervals");
+ *   - every batch, a preprocess kernel evaluates the endpoints against the
+ *     batch metadata and writes an Execution Descriptor for the forward and
+ *     the backward pass (section 3.3 "Online Efficient Mask Attention
+ *     Execution"): an Interval Table of visible [start,end) intervals padded
+ *     with zero-length intervals, plus two-bit-per-tile state bitmaps
+ *     (section 3.3.1 "Execution Descriptor");
+ *   - the attention kernels skip empty tiles, run full tiles without a mask
+ *     and check visibility with unsigned endpoint compares only in partial
+ *     tiles, replacing invisible scores by -inf before the online softmax
+ *     (section 3.3.2 "Descriptor-Guided Attention Execution").
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller owns every device buffer (tensors, metadata, the
+ *     descriptor buffer, the backward workspace) and the stream.  The library
+ *     owns only the opaque host handles cm_spec and cm_desc.  It never
+ *     allocates device memory.
+ *   - Streams: `cm_stream` is a hipStream_t (NULL = the default stream).  The
+ *     hot calls (cm_build_descriptor, cm_attn_fwd, cm_attn_bwd and
+ *     cm_attn_bwd_stage) only enqueue kernels on it; they never synchronise.
+ *   - Errors: every call returns a cm_status.  A negative status means the
+ *     call did nothing (no kernel launched, no output written); the detail is
+ *     in cm_last_error() (thread-local, valid until the next call on the same
+ *     thread).  No C++ exception crosses this boundary.
+ *   - Errors found in the metadata on the device are not reported by the
+ *     status: the preprocess kernel sets bits in the descriptor's header word
+ *     13 and in sample_err[b], and gives that sample no visible pair at all.
+ *
+ * Descriptor byte layout (uint32 words, every section at a multiple of 256
+ * bytes, gaps zero; Tq_f = ceil(N/fwd_q), Tk_f = ceil(N/fwd_k),
+ * Tk_b = ceil(N/bwd_k), Tq_b = ceil(N/bwd_q)):
+ *   header[16]     0x31444D43, B, N, K_r, K_c, fwd_q, fwd_k, bwd_k, bwd_q,
+ *                  Tq_f, Tk_f, Tk_b, Tq_b, OR of sample_err, seg_cap, 0
+ *   sample_err[B]  CM_MD_* bits of each sample's metadata
+ *   row_tkmax[B][Tq_f]   largest run count among a forward query tile's rows
+ *   col_tkmax[B][Tk_b]   largest run count among a backward key tile's columns
+ *   fbm[B][Tq_f][ceil(Tk_f/16)]  forward Tile-State Bitmap (query tile major)
+ *   bbm[B][Tk_b][ceil(Tq_b/16)]  backward Tile-State Bitmap (key tile major)
+ *   row_iv[B][N][K_r][2]  per query row: visible key runs [start,end)
+ *   col_iv[B][N][K_c][2]  per key column: visible query-row runs [start,end)
+ * Tile codes: 0 empty, 1 full, 2 partial; tile c sits at bits 2*(c%16) of word
+ * c/16.  Runs are maximal, ascending, and padded with (0,0) at the tail.  The
+ * descriptor is per sample and shared by all heads.
+ */
+#ifndef COMPILEMASK_H
+#define COMPILEMASK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cm_spec cm_spec;  /* compiled MaskSpec (host, immutable)        */
+typedef struct cm_desc cm_desc;  /* host handle over a caller-owned descriptor */
+typedef void* cm_stream;         /* hipStream_t                                */
+
+typedef enum cm_status {
+  CM_OK = 0,
+  CM_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  CM_ERR_INVALID = -2,     /* an argument is out of range                     */
+  CM_ERR_PARSE = -3,       /* the spec text does not parse or lower           */
+  CM_ERR_MISMATCH = -4,    /* descriptor and spec/arguments do not belong together */
+  CM_ERR_UNSUPPORTED = -5, /* no kernel for this head dim / tile shape        */
+  CM_ERR_SIZE = -6,        /* a caller buffer is too small                    */
+  CM_ERR_HIP = -7          /* the HIP runtime reported an error               */
+} cm_status;
+
+/* Metadata error bits (descriptor header word 13 and sample_err[b]). */
+#define CM_MD_NSEG 1u          /* n_seg outside [0, seg_cap]                   */
+#define CM_MD_BOUNDS_ORDER 2u  /* a used boundary is smaller than the one before */
+#define CM_MD_BOUNDS_RANGE 4u  /* a used boundary lies outside [0, N]          */
+#define CM_MD_REF_RANGE 8u     /* a used reference lies outside [-1, n_seg)    */
+
+#define CM_DESC_MAGIC 0x31444D43u
+
+/* Tile shapes of the two descriptor grids.  Forward grid: fwd_q query rows x
+ * fwd_k keys.  Backward grid: bwd_k keys x bwd_q query rows.  The preprocess
+ * accepts any positive sizes; the attention kernels accept (fwd_q, fwd_k) in
+ * {(64,64), (128,64)} and (bwd_k, bwd_q) in {(64,64), (128,64)}. */
+typedef struct cm_tiles {
+  int32_t fwd_q, fwd_k, bwd_k, bwd_q;
+} cm_tiles;
+
+/* Batch metadata: device int32 arrays, caller-owned, read by
+ * cm_build_descriptor (CompileMask paper summary, section 1: mask boundaries
+ * depend on sequence lengths and segment boundaries).
+ *   scalars    [B][n_scalars]  the spec's `param` values, in declaration order
+ *   seg_bounds [B][seg_cap+1]  segment s of sample b is
+ *                              [seg_bounds[b][s], seg_bounds[b][s+1]), s < n_seg[b]
+ *   n_seg      [B]
+ *   refs       [B][seg_cap][n_refs]  referenced segment ids, -1 = none
+ * A pointer may be NULL when its array is empty (n_scalars == 0, seg_cap == 0
+ * or n_refs == 0). */
+typedef struct cm_metadata {
+  const int32_t* scalars;
+  const int32_t* seg_bounds;
+  const int32_t* n_seg;
+  const int32_t* refs;
+  int32_t n_scalars;
+  int32_t n_refs;
+} cm_metadata;
+
+/* Attention shapes.  q, k, v, o, dO, dq, dk, dv are bf16 [B][H][N][d] with
+ * the last dimension contiguous and element strides stride_b, stride_h,
+ * stride_n (all three 0 = contiguous [B,H,N,d]); lse is fp32 [B][H][N]
+ * contiguous.  scale 0 means 1/sqrt(d).  causal = 1 selects the maskless
+ * causal path (row i sees keys 0..i, tile states from indices, no descriptor:
+ * desc may be NULL); causal = 0 uses the descriptor. */
+typedef struct cm_attn_args {
+  int32_t B, H, N, d;
+  int64_t stride_b, stride_h, stride_n;
+  float scale;
+  int32_t causal;
+} cm_attn_args;
+
+/* ---- offline: MaskSpec -> symbolic endpoints (section 3.2.2) ------------ */
+
+/* Parse and lower a MaskSpec text (grammar in the package's spec docs: one
+ * `forward` and one `backward` section of `region NAME: GUARD => RULE`
+ * lines).  Lowering: AST, negation pushed to atoms, DNF, one interval per
+ * conjunct, canonicalisation (redundant bounds dropped, provably empty
+ * conjuncts dropped, conjuncts with the same interval merged, adjacent
+ * intervals merged when provable over the whole Region).  On success *out
+ * owns a new spec (free with cm_spec_free); it is immutable and may be
+ * shared by threads.  CM_ERR_PARSE on any syntax or lowering error. */
+cm_status cm_spec_compile(const char* text, cm_spec** out);
+void cm_spec_free(cm_spec* spec);
+
+/* Interval-table widths the spec needs for a segment capacity: K_row (query
+ * rows, forward) and K_col (key columns, backward) = the largest slot count
+ * of any Region of that direction; an `exists` slot counts seg_cap slots.
+ * Also the number of scalars and references the metadata must carry. */
+cm_status cm_spec_info(const cm_spec* spec, int32_t seg_cap, int32_t* K_row, int32_t* K_col,
+                       int32_t* n_scalars, int32_t* n_refs);
+
+/* Human-readable listing of the lowered program (regions, slots, bounds,
+ * conditions) into buf (NUL-terminated, truncated to len).  *needed gets the
+ * full length + 1 when non-NULL. */
+cm_status cm_spec_dump(const cm_spec* spec, char* buf, size_t len, size_t* needed);
+
+/* Evaluate one index on the host (inspection aid; not used by any other
+ * entry point): the visible runs of query row `index` (direction 0) or key
+ * column `index` (direction 1) of ONE sample whose metadata is given in host
+ * arrays (scalars[n_scalars], seg_bounds[seg_cap+1], refs[seg_cap][n_refs]).
+ * Writes up to `cap` pairs to runs[2*cap] and their count to *n_runs.
+ * Metadata errors give *md_err != 0 and no runs. */
+cm_status cm_spec_eval_host(const cm_spec* spec, int32_t direction, int32_t N, int32_t index,
+                            const int32_t* scalars, int32_t n_scalars, const int32_t* seg_bounds,
+                            int32_t n_seg, int32_t seg_cap, const int32_t* refs, int32_t n_refs,
+                            uint32_t* runs, int32_t cap, int32_t* n_runs, uint32_t* md_err);
+
+/* ---- descriptor memory (caller-owned) ---------------------------------- */
+
+/* Bytes of a descriptor for (spec, B, N, seg_cap, tiles). */
+cm_status cm_desc_size(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap,
+                       const cm_tiles* tiles, size_t* bytes);
+
+/* Bind a caller-owned device buffer of at least cm_desc_size() bytes to a new
+ * descriptor handle and zero it (synchronously, once).  The handle does not
+ * own dev_buf; free the handle with cm_desc_free and the buffer yourself. */
+cm_status cm_desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap,
+                       const cm_tiles* tiles, void* dev_buf, size_t bytes, cm_desc** out);
+void cm_desc_free(cm_desc* desc);
+
+/* Byte offsets of the descriptor sections, in layout order: header,
+ * sample_err, row_tkmax, col_tkmax, fbm, bbm, row_iv, col_iv; then the
+ * total size.  offsets must hold 9 entries. */
+cm_status cm_desc_offsets(const cm_desc* desc, size_t* offsets);
+
+/* ---- online, every batch (section 3.3) --------------------------------- */
+
+/* One preprocess kernel launch: evaluate the compiled endpoints of `spec`
+ * against `md` and write the whole descriptor (header, both interval tables,
+ * both bitmaps, per-tile run maxima, error words).  desc must come from
+ * cm_desc_init with the same spec.  Asynchronous on `stream`. */
+cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_desc* desc,
+                              cm_stream stream);
+
+/* Forward: o (bf16) and lse (fp32, natural log; -inf for a row with no
+ * visible key, whose o row is 0).  Requires d in {64, 128} and a descriptor
+ * whose forward tiles are supported.  Asynchronous on `stream`. */
+cm_status cm_attn_fwd(const cm_attn_args* args, const void* q, const void* k, const void* v,
+                      const cm_desc* desc, void* o, float* lse, cm_stream stream);
+
+/* Bytes of fp32 workspace cm_attn_bwd needs (rowsum(dO * O) per row). */
+cm_status cm_attn_bwd_workspace(const cm_attn_args* args, size_t* bytes);
+
+/* Backward from the forward's o and lse: dq, dk, dv (bf16).  Three kernels on
+ * `stream`: D = rowsum(dO * O); dK/dV per key tile over the query tiles that
+ * the backward bitmap marks non-empty (column runs in partial tiles); dQ per
+ * query tile over the forward bitmap (row runs).  Deterministic (no atomics). */
+cm_status cm_attn_bwd(const cm_attn_args* args, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dO, const cm_desc* desc,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      cm_stream stream);
+
+/* One of the three backward kernels alone, same arguments as cm_attn_bwd
+ * (stage 0: D, stage 1: dK/dV, stage 2: dQ), for per-kernel timing.  Running
+ * stages 0, 1, 2 in order equals cm_attn_bwd. */
+cm_status cm_attn_bwd_stage(int32_t stage, const cm_attn_args* args, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* dO,
+                            const cm_desc* desc, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, cm_stream stream);
+
+/* ---- diagnostics -------------------------------------------------------- */
+const char* cm_status_str(cm_status status);
+const char* cm_last_error(void);
+/* Library version string and the gfx target it was built for. */
+const char* cm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COMPILEMASK_H */

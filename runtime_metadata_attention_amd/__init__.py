@@ -1,0 +1,317 @@
+"""Python binding of libcompilemask (CompileMask hot path for MI355X / gfx950).
+
+The functions below carry the C ABI's names (include/compilemask.h) and only
+marshal arguments: every step of the path runs in the library's HIP kernels.
+PyTorch supplies device memory and the stream.  Importing works without a
+GPU (the spec compiler and the host inspection call run on the CPU), but the
+library itself must be built: there is no fallback of any kind.
+
+    spec = cm_spec_compile(text)
+    desc = Descriptor(spec, B, N, seg_cap, tiles, device)     # cm_desc_size + cm_desc_init
+    cm_build_descriptor(spec, device_metadata(md, device), desc)
+    cm_attn_fwd(attn_args(q), q, k, v, desc, o, lse)
+    cm_attn_bwd(attn_args(q), q, k, v, o, lse, do, desc, dq, dk, dv, ws)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libcompilemask.so")
+
+CM_OK = 0
+STATUS = {0: "CM_OK", -1: "CM_ERR_NULL", -2: "CM_ERR_INVALID", -3: "CM_ERR_PARSE", -4: "CM_ERR_MISMATCH",
+          -5: "CM_ERR_UNSUPPORTED", -6: "CM_ERR_SIZE", -7: "CM_ERR_HIP"}
+SECTIONS = ("header", "sample_err", "row_tkmax", "col_tkmax", "fbm", "bbm", "row_iv", "col_iv", "total")
+# every symbol include/compilemask.h declares
+EXPORTS = ("cm_spec_compile", "cm_spec_free", "cm_spec_info", "cm_spec_dump", "cm_spec_eval_host",
+           "cm_desc_size", "cm_desc_init", "cm_desc_free", "cm_desc_offsets", "cm_build_descriptor",
+           "cm_attn_fwd", "cm_attn_bwd_workspace", "cm_attn_bwd", "cm_attn_bwd_stage",
+           "cm_status_str", "cm_last_error", "cm_version")
+
+
+class CompileMaskError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+
+
+class cm_tiles(ctypes.Structure):
+    _fields_ = [("fwd_q", ctypes.c_int32), ("fwd_k", ctypes.c_int32),
+                ("bwd_k", ctypes.c_int32), ("bwd_q", ctypes.c_int32)]
+
+
+class cm_metadata(ctypes.Structure):
+    _fields_ = [("scalars", ctypes.c_void_p), ("seg_bounds", ctypes.c_void_p), ("n_seg", ctypes.c_void_p),
+                ("refs", ctypes.c_void_p), ("n_scalars", ctypes.c_int32), ("n_refs", ctypes.c_int32)]
+
+
+class cm_attn_args(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libcompilemask.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m runtime_metadata_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    sig = {
+        "cm_spec_compile": (I32, [ctypes.c_char_p, P(VP)]),
+        "cm_spec_free": (None, [VP]),
+        "cm_spec_info": (I32, [VP, I32, P(I32), P(I32), P(I32), P(I32)]),
+        "cm_spec_dump": (I32, [VP, ctypes.c_char_p, SZ, P(SZ)]),
+        "cm_spec_eval_host": (I32, [VP, I32, I32, I32, VP, I32, VP, I32, I32, VP, I32, VP, I32, P(I32),
+                                    P(ctypes.c_uint32)]),
+        "cm_desc_size": (I32, [VP, I32, I32, I32, P(cm_tiles), P(SZ)]),
+        "cm_desc_init": (I32, [VP, I32, I32, I32, P(cm_tiles), VP, SZ, P(VP)]),
+        "cm_desc_free": (None, [VP]),
+        "cm_desc_offsets": (I32, [VP, P(SZ)]),
+        "cm_build_descriptor": (I32, [VP, P(cm_metadata), VP, VP]),
+        "cm_attn_fwd": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP]),
+        "cm_attn_bwd_workspace": (I32, [P(cm_attn_args), P(SZ)]),
+        "cm_attn_bwd": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+        "cm_attn_bwd_stage": (I32, [I32, P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+        "cm_status_str": (ctypes.c_char_p, [I32]),
+        "cm_last_error": (ctypes.c_char_p, []),
+        "cm_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(st: int, where: str):
+    if st != CM_OK:
+        raise CompileMaskError(st, where, library().cm_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+# ------------------------------------------------------------------ spec
+
+class Spec:
+    """Owner of a compiled cm_spec handle."""
+
+    def __init__(self, handle: int, text: str):
+        self.handle = handle
+        self.text = text
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.cm_spec_free(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+
+def cm_spec_compile(text: str) -> Spec:
+    h = ctypes.c_void_p()
+    _check(library().cm_spec_compile(text.encode(), ctypes.byref(h)), "cm_spec_compile")
+    return Spec(h.value, text)
+
+
+def cm_spec_info(spec: Spec, seg_cap: int) -> Tuple[int, int, int, int]:
+    """(K_row, K_col, n_scalars, n_refs)."""
+    out = [ctypes.c_int32() for _ in range(4)]
+    _check(library().cm_spec_info(spec.handle, seg_cap, *[ctypes.byref(x) for x in out]), "cm_spec_info")
+    return tuple(x.value for x in out)
+
+
+def cm_spec_dump(spec: Spec) -> str:
+    need = ctypes.c_size_t()
+    _check(library().cm_spec_dump(spec.handle, None, 0, ctypes.byref(need)), "cm_spec_dump")
+    buf = ctypes.create_string_buffer(need.value)
+    _check(library().cm_spec_dump(spec.handle, buf, need.value, None), "cm_spec_dump")
+    return buf.value.decode()
+
+
+def cm_spec_eval_host(spec: Spec, direction: int, N: int, index: int, scalars: Sequence[int],
+                      seg_bounds: Sequence[int], n_seg: int, refs, n_refs: int, cap: int = 4096):
+    """Visible runs of one query row (direction 0) or key column (1) of one
+    sample, evaluated on the host from the lowered program.  Returns
+    (list of (start, end), metadata error bits)."""
+    import numpy as np
+
+    sc = np.ascontiguousarray(np.asarray(scalars, np.int32).ravel())
+    sb = np.ascontiguousarray(np.asarray(seg_bounds, np.int32).ravel())
+    rf = np.ascontiguousarray(np.asarray(refs, np.int32).ravel())
+    seg_cap = max(0, len(sb) - 1)
+    runs = (ctypes.c_uint32 * (2 * cap))()
+    n = ctypes.c_int32()
+    err = ctypes.c_uint32()
+    _check(library().cm_spec_eval_host(
+        spec.handle, direction, N, index,
+        sc.ctypes.data if sc.size else None, len(sc),
+        sb.ctypes.data if sb.size else None, n_seg, seg_cap,
+        rf.ctypes.data if rf.size else None, n_refs,
+        runs, cap, ctypes.byref(n), ctypes.byref(err)), "cm_spec_eval_host")
+    return [(runs[2 * q], runs[2 * q + 1]) for q in range(n.value)], err.value
+
+
+# ------------------------------------------------------------------ descriptor
+
+def make_tiles(tiles) -> cm_tiles:
+    if isinstance(tiles, cm_tiles):
+        return tiles
+    return cm_tiles(*[int(x) for x in tiles])
+
+
+def cm_desc_size(spec: Spec, B: int, N: int, seg_cap: int, tiles) -> int:
+    out = ctypes.c_size_t()
+    _check(library().cm_desc_size(spec.handle, B, N, seg_cap, ctypes.byref(make_tiles(tiles)), ctypes.byref(out)),
+           "cm_desc_size")
+    return out.value
+
+
+class Descriptor:
+    """A cm_desc handle over a torch uint8 device buffer it keeps alive."""
+
+    def __init__(self, spec: Spec, B: int, N: int, seg_cap: int, tiles, device=None, buffer=None):
+        import torch
+
+        self.spec = spec
+        self.B, self.N, self.seg_cap = B, N, seg_cap
+        self.tiles = tuple(int(x) for x in (tiles if not isinstance(tiles, cm_tiles) else
+                                            (tiles.fwd_q, tiles.fwd_k, tiles.bwd_k, tiles.bwd_q)))
+        self.bytes = cm_desc_size(spec, B, N, seg_cap, self.tiles)
+        if buffer is None:
+            buffer = torch.empty(self.bytes, dtype=torch.uint8, device=device or "cuda")
+        self.buffer = buffer
+        h = ctypes.c_void_p()
+        _check(library().cm_desc_init(spec.handle, B, N, seg_cap, ctypes.byref(make_tiles(self.tiles)),
+                                      ctypes.c_void_p(_ptr(buffer)), buffer.numel() * buffer.element_size(),
+                                      ctypes.byref(h)), "cm_desc_init")
+        self.handle = h.value
+        K = cm_spec_info(spec, seg_cap)
+        self.K_r, self.K_c = K[0], K[1]
+
+    def offsets(self):
+        return cm_desc_offsets(self)
+
+    def words(self):
+        """The descriptor as a host numpy uint32 array (synchronises)."""
+        return self.buffer[: self.bytes].view(__import__("torch").int32).cpu().numpy().view("uint32")
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.cm_desc_free(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+
+def cm_desc_offsets(desc: Descriptor):
+    out = (ctypes.c_size_t * 9)()
+    _check(library().cm_desc_offsets(desc.handle, out), "cm_desc_offsets")
+    return dict(zip(SECTIONS, list(out)))
+
+
+class DeviceMetadata:
+    """Device int32 copies of a metadata object (scalars, seg_bounds, n_seg, refs)."""
+
+    def __init__(self, md, device="cuda"):
+        import torch
+
+        def up(a):
+            t = torch.as_tensor(a).to(torch.int32).contiguous()
+            return t.to(device) if t.numel() else None
+
+        self.scalars = up(md.scalars)
+        self.seg_bounds = up(md.seg_bounds)
+        self.n_seg = up(md.n_seg)
+        self.refs = up(md.refs)
+        self.n_scalars = int(md.scalars.shape[1])
+        self.n_refs = int(md.refs.shape[2]) if md.refs.ndim == 3 else 0
+
+    def struct(self) -> cm_metadata:
+        return cm_metadata(_ptr(self.scalars), _ptr(self.seg_bounds), _ptr(self.n_seg), _ptr(self.refs),
+                           self.n_scalars, self.n_refs)
+
+
+def device_metadata(md, device="cuda") -> DeviceMetadata:
+    return DeviceMetadata(md, device)
+
+
+def cm_build_descriptor(spec: Spec, md: DeviceMetadata, desc: Descriptor, stream=None):
+    m = md.struct()
+    _check(library().cm_build_descriptor(spec.handle, ctypes.byref(m), desc.handle, _stream(stream)),
+           "cm_build_descriptor")
+
+
+# ------------------------------------------------------------------ attention
+
+def attn_args(q, causal: bool = False, scale: float = 0.0) -> cm_attn_args:
+    """cm_attn_args from a [B, H, N, d] bf16 tensor's shape and strides."""
+    B, H, N, d = q.shape
+    sb, sh, sn, sd = q.stride()
+    if sd != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return cm_attn_args(B, H, N, d, sb, sh, sn, float(scale), 1 if causal else 0)
+
+
+def _desc_handle(desc):
+    return None if desc is None else desc.handle
+
+
+def cm_attn_fwd(args: cm_attn_args, q, k, v, desc, o, lse, stream=None):
+    _check(library().cm_attn_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _desc_handle(desc), _ptr(o),
+                                 _ptr(lse), _stream(stream)), "cm_attn_fwd")
+
+
+def cm_attn_bwd_workspace(args: cm_attn_args) -> int:
+    out = ctypes.c_size_t()
+    _check(library().cm_attn_bwd_workspace(ctypes.byref(args), ctypes.byref(out)), "cm_attn_bwd_workspace")
+    return out.value
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def cm_attn_bwd(args: cm_attn_args, q, k, v, o, lse, do, desc, dq, dk, dv, workspace, stream=None):
+    _check(library().cm_attn_bwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                 _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 _nbytes(workspace), _stream(stream)), "cm_attn_bwd")
+
+
+def cm_attn_bwd_stage(stage: int, args: cm_attn_args, q, k, v, o, lse, do, desc, dq, dk, dv, workspace, stream=None):
+    _check(library().cm_attn_bwd_stage(stage, ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _ptr(do), _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                       _nbytes(workspace), _stream(stream)), "cm_attn_bwd_stage")
+
+
+def cm_status_str(status: int) -> str:
+    return library().cm_status_str(status).decode()
+
+
+def cm_last_error() -> str:
+    return library().cm_last_error().decode()
+
+
+def cm_version() -> str:
+    return library().cm_version().decode()
+
+
+from . import specs  # noqa: E402,F401

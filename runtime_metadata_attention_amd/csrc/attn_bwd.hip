@@ -1,0 +1,567 @@
+// attn_bwd.hip -- descriptor-guided attention backward.
+//
+// Training throughput counts forward plus backward (CompileMask paper summary,
+// section 1), and the backward has its own descriptor direction (section 3.3
+// "Online Efficient Mask Attention Execution": forward and backward use
+// separate rules so that their intervals follow each pass's traversal).
+//
+// Three kernels, no atomics, deterministic:
+//   D    : D[q] = rowsum(dO[q] * O[q]) in fp32.
+//   dK/dV: one work-group per key tile (bwd_k keys), looping over the query
+//          tiles its backward bitmap row marks non-empty.  Scores are kept
+//          with keys in the columns (lane = key), so each lane's column runs
+//          (visible query rows) are loop-invariant registers.
+//            S = Q K^T, P = exp(S - lse) (masked in partial tiles),
+//            dV^T += dO^T P, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS.
+//   dQ   : one work-group per query tile (fwd_q rows) over the forward
+//          bitmap row and the row runs (lane = query):
+//            S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+// K^T, V^T of the work-group's own keys (dK/dV) and Q^T, dO^T of its own
+// queries (dQ) stay in registers; the streamed tiles are staged in LDS
+// row-major and also read transposed (ds_read_b64_tr_b16).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "attn_common.h"
+#include "internal.h"
+
+namespace cm {
+namespace {
+
+using namespace attn;
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* lse;
+  const float* D;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* Dout;
+  int64_t sb, sh, sn;
+  int32_t B, H, N, d;
+  float scale, scale_log2;
+  // forward grid (dQ)
+  int32_t Tq_f, Tk_f, Wf;
+  const uint32_t* fbm;
+  const uint2* row_iv;
+  int32_t K_r;
+  const uint32_t* row_tkmax;
+  // backward grid (dK/dV)
+  int32_t Tk_b, Tq_b, Wb;
+  const uint32_t* bbm;
+  const uint2* col_iv;
+  int32_t K_c;
+  const uint32_t* col_tkmax;
+};
+
+constexpr int MAXR = 4;
+constexpr int BQ = 64;  // query rows per step of the dK/dV kernel
+constexpr int BN = 64;  // keys per step of the dQ kernel
+
+// ------------------------------------------------------------------ D
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPB = 256 / LPR;      // rows per block
+  const int t = threadIdx.x;
+  const int64_t row = int64_t(blockIdx.x) * RPB + t / LPR;
+  const int64_t total = int64_t(p.B) * p.H * p.N;
+  float acc = 0.f;
+  if (row < total) {
+    const int n = int(row % p.N);
+    const int64_t bh = row / p.N;
+    const int hh = int(bh % p.H), bb = int(bh / p.H);
+    const size_t off = size_t(bb) * p.sb + size_t(hh) * p.sh + size_t(n) * p.sn + (t % LPR) * 8;
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(p.o + off));
+    const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(p.dO + off));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += float(a[e]) * float(b[e]);
+  }
+#pragma unroll
+  for (int s = LPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
+  if (row < total && (t % LPR) == 0) p.Dout[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK / dV
+
+template <int D, int BK, bool CAUSAL>
+__global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NT = BK * 2;
+  constexpr int LDSTR = D + 8;
+  constexpr int CHUNKS = BQ * D / 8;
+  constexpr int LPT = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * LDSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[BQ * LDSTR];  // dO tile
+  __shared__ __attribute__((aligned(16))) float sL[BQ];             // lse * log2(e); +inf = no row
+  __shared__ __attribute__((aligned(16))) float sD[BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, lk = lane & 31;
+  const int kt = p.Tk_b - 1 - int(blockIdx.x);
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int N = p.N;
+  const int k0 = kt * BK;
+  const int key = k0 + wave * 32 + lk;
+  const bool kvalid = key < N;
+  const size_t base = size_t(b) * p.sb + size_t(head) * p.sh;
+  const uint16_t* Qp = p.q + base;
+  const uint16_t* Op = p.dO + base;
+  const size_t rbase = (size_t(b) * p.H + head) * N;
+
+  bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    uint4 uk = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
+    if (kvalid) {
+      uk = *reinterpret_cast<const uint4*>(p.k + base + size_t(key) * p.sn + 16 * c + 8 * h);
+      uv = *reinterpret_cast<const uint4*>(p.v + base + size_t(key) * p.sn + 16 * c + 8 * h);
+    }
+    kreg[c] = as_bf16x8(uk);
+    vreg[c] = as_bf16x8(uv);
+  }
+
+  int nr;
+  uint32_t rs[MAXR], rl[MAXR];
+  const uint2* myruns = nullptr;
+  if (CAUSAL) {
+    nr = 1;
+    rs[0] = uint32_t(key); rl[0] = uint32_t(N - key);
+#pragma unroll
+    for (int r = 1; r < MAXR; ++r) { rs[r] = 0; rl[r] = 0; }
+  } else {
+    nr = int(uniform(p.col_tkmax[size_t(b) * p.Tk_b + kt]));
+    myruns = p.col_iv + (size_t(b) * N + (kvalid ? key : 0)) * p.K_c;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      uint2 v = make_uint2(0, 0);
+      if (r < nr && kvalid) v = myruns[r];
+      rs[r] = v.x;
+      rl[r] = v.y - v.x;
+    }
+  }
+
+  f32x16 adv[D / 32], adk[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) { adv[db] = f32x16{}; adk[db] = f32x16{}; }
+
+  TileIter it;
+  int cnext = 0, clast = 0;
+  if (!CAUSAL) it.init(p.bbm + (size_t(b) * p.Tk_b + kt) * p.Wb, p.Wb);
+  else { cnext = k0 / BQ; clast = p.Tq_b - 1; }
+  auto next_tile = [&](int& tile, int& state) -> bool {
+    if (CAUSAL) {
+      if (cnext > clast) return false;
+      tile = cnext++;
+      state = (tile * BQ >= k0 + BK - 1) ? 1 : 2;
+      return true;
+    }
+    return it.next(tile, state);
+  };
+
+  uint4 pq[LPT], po[LPT];
+  float pl = 0.f, pd = 0.f;
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int c = tid + NT * j;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int qi = tile * BQ + row;
+      if (qi < N) {
+        pq[j] = *reinterpret_cast<const uint4*>(Qp + size_t(qi) * p.sn + col);
+        po[j] = *reinterpret_cast<const uint4*>(Op + size_t(qi) * p.sn + col);
+      } else {
+        pq[j] = make_uint4(0, 0, 0, 0);
+        po[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < BQ) {
+      const int qi = tile * BQ + tid;
+      float l = INFINITY, dd = 0.f;
+      if (qi < N) {
+        const float x = p.lse[rbase + qi];
+        l = (x == -INFINITY) ? INFINITY : x * kLog2e;
+        dd = p.D[rbase + qi];
+      }
+      pl = l;
+      pd = dd;
+    }
+  };
+
+  int tile = 0, state = 0;
+  bool have = next_tile(tile, state);
+  if (have) load_tile(tile);
+  const int g = lane >> 4, gi = lane & 15;
+  while (have) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int c = tid + NT * j;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(sQ + row * LDSTR + col) = pq[j];
+      *reinterpret_cast<uint4*>(sO + row * LDSTR + col) = po[j];
+    }
+    if (tid < BQ) { sL[tid] = pl; sD[tid] = pd; }
+    __syncthreads();
+    const int ct = tile, cs = state;
+    have = next_tile(tile, state);
+    if (have) load_tile(tile);
+
+    // S = Q K^T and dP = dO V^T: two 32-row blocks, lane = key column
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        bf16x8 aq = lds_read_b128(sQ + (qb * 32 + lk) * LDSTR + 16 * c + 8 * h);
+        s[qb] = mfma32(aq, kreg[c], s[qb]);
+        bf16x8 ao = lds_read_b128(sO + (qb * 32 + lk) * LDSTR + 16 * c + 8 * h);
+        dp[qb] = mfma32(ao, vreg[c], dp[qb]);
+      }
+    }
+    const bool masked = (cs == 2) || ((ct + 1) * BQ > N);
+    const uint32_t qbase = uint32_t(ct * BQ + 4 * h);
+    bf16x8 pb[4], db8[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const float4 l4 = *reinterpret_cast<const float4*>(sL + qb * 32 + vg * 8 + 4 * h);
+        const float4 d4 = *reinterpret_cast<const float4*>(sD + qb * 32 + vg * 8 + 4 * h);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = vg * 4 + e;
+          float pe = __builtin_amdgcn_exp2f(s[qb][v] * p.scale_log2 - lv[e]);
+          if (masked) {
+            const uint32_t qo = qbase + uint32_t(qb * 32 + vg * 8 + e);
+            bool vis = false;
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r) vis = vis || (qo - rs[r] < rl[r]);
+            if (!CAUSAL && nr > MAXR) {
+              for (int r = MAXR; r < nr; ++r) {
+                uint2 rr = kvalid ? myruns[r] : make_uint2(0, 0);
+                vis = vis || (qo - rr.x < rr.y - rr.x);
+              }
+            }
+            if (!vis) pe = 0.f;
+          }
+          const float ds = pe * (dp[qb][v] - dv4[e]);
+          const int qc = qb * 2 + (v >> 3), ee = v & 7;
+          pb[qc][ee] = (__bf16)pe;
+          db8[qc][ee] = (__bf16)ds;
+        }
+      }
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS   (k = query, in the score-register order)
+#pragma unroll
+    for (int qc = 0; qc < 4; ++qc) {
+      const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
+#pragma unroll
+      for (int dbk = 0; dbk < D / 32; ++dbk) {
+        const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
+        const uint16_t* po1 = sO + kr * LDSTR + col;
+        bf16x8 ao = cat4(lds_read_tr4(po1), lds_read_tr4(po1 + 8 * LDSTR));
+        adv[dbk] = mfma32(ao, pb[qc], adv[dbk]);
+        const uint16_t* pq1 = sQ + kr * LDSTR + col;
+        bf16x8 aq = cat4(lds_read_tr4(pq1), lds_read_tr4(pq1 + 8 * LDSTR));
+        adk[dbk] = mfma32(aq, db8[qc], adk[dbk]);
+      }
+    }
+  }
+
+  if (kvalid) {
+    uint16_t* dKp = p.dk + base + size_t(key) * p.sn;
+    uint16_t* dVp = p.dv + base + size_t(key) * p.sn;
+#pragma unroll
+    for (int dbk = 0; dbk < D / 32; ++dbk) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = (__bf16)(adk[dbk][vg * 4 + e] * p.scale);
+          v4[e] = (__bf16)(adv[dbk][vg * 4 + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dKp + dbk * 32 + vg * 8 + 4 * h) = k4;
+        *reinterpret_cast<bf16x4*>(dVp + dbk * 32 + vg * 8 + 4 * h) = v4;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <int D, int BM, bool CAUSAL>
+__global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = BM / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LDSTR = D + 8;
+  constexpr int CHUNKS = BN * D / 8;
+  constexpr int LPT = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * LDSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * LDSTR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, lq = lane & 31;
+  const int qt = p.Tq_f - 1 - int(blockIdx.x);
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int N = p.N;
+  const int q0 = qt * BM;
+  const int q = q0 + wave * 32 + lq;
+  const bool qvalid = q < N;
+  const size_t base = size_t(b) * p.sb + size_t(head) * p.sh;
+  const uint16_t* Kp = p.k + base;
+  const uint16_t* Vp = p.v + base;
+  const size_t rbase = (size_t(b) * p.H + head) * N;
+
+  bf16x8 qreg[D / 16], oreg[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    uint4 uq = make_uint4(0, 0, 0, 0), uo = make_uint4(0, 0, 0, 0);
+    if (qvalid) {
+      uq = *reinterpret_cast<const uint4*>(p.q + base + size_t(q) * p.sn + 16 * c + 8 * h);
+      uo = *reinterpret_cast<const uint4*>(p.dO + base + size_t(q) * p.sn + 16 * c + 8 * h);
+    }
+    qreg[c] = as_bf16x8(uq);
+    oreg[c] = as_bf16x8(uo);
+  }
+  float lse2 = INFINITY, Dq = 0.f;
+  if (qvalid) {
+    const float x = p.lse[rbase + q];
+    lse2 = (x == -INFINITY) ? INFINITY : x * kLog2e;
+    Dq = p.D[rbase + q];
+  }
+
+  int nr;
+  uint32_t rs[MAXR], rl[MAXR];
+  const uint2* myruns = nullptr;
+  if (CAUSAL) {
+    nr = 1;
+    rs[0] = 0; rl[0] = uint32_t(q + 1);
+#pragma unroll
+    for (int r = 1; r < MAXR; ++r) { rs[r] = 0; rl[r] = 0; }
+  } else {
+    nr = int(uniform(p.row_tkmax[size_t(b) * p.Tq_f + qt]));
+    myruns = p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      uint2 v = make_uint2(0, 0);
+      if (r < nr && qvalid) v = myruns[r];
+      rs[r] = v.x;
+      rl[r] = v.y - v.x;
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  TileIter it;
+  int cnext = 0, clast = 0;
+  if (!CAUSAL) it.init(p.fbm + (size_t(b) * p.Tq_f + qt) * p.Wf, p.Wf);
+  else clast = min(p.Tk_f - 1, (q0 + BM - 1) / BN);
+  auto next_tile = [&](int& tile, int& state) -> bool {
+    if (CAUSAL) {
+      if (cnext > clast) return false;
+      tile = cnext++;
+      state = ((tile + 1) * BN - 1 <= q0) ? 1 : 2;
+      return true;
+    }
+    return it.next(tile, state);
+  };
+
+  uint4 pk[LPT], pv[LPT];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int c = tid + NT * j;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int kk = tile * BN + row;
+      if (kk < N) {
+        pk[j] = *reinterpret_cast<const uint4*>(Kp + size_t(kk) * p.sn + col);
+        pv[j] = *reinterpret_cast<const uint4*>(Vp + size_t(kk) * p.sn + col);
+      } else {
+        pk[j] = make_uint4(0, 0, 0, 0);
+        pv[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int tile = 0, state = 0;
+  bool have = next_tile(tile, state);
+  if (have) load_tile(tile);
+  const int g = lane >> 4, gi = lane & 15;
+  while (have) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int c = tid + NT * j;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(sK + row * LDSTR + col) = pk[j];
+      *reinterpret_cast<uint4*>(sV + row * LDSTR + col) = pv[j];
+    }
+    __syncthreads();
+    const int ct = tile, cs = state;
+    have = next_tile(tile, state);
+    if (have) load_tile(tile);
+
+    // S^T = K Q^T and dP^T = V dO^T (lane = query)
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 ak = lds_read_b128(sK + (kb * 32 + lq) * LDSTR + 16 * c + 8 * h);
+        s[kb] = mfma32(ak, qreg[c], s[kb]);
+        bf16x8 av = lds_read_b128(sV + (kb * 32 + lq) * LDSTR + 16 * c + 8 * h);
+        dp[kb] = mfma32(av, oreg[c], dp[kb]);
+      }
+    }
+    const bool masked = (cs == 2) || ((ct + 1) * BN > N);
+    const uint32_t kbase = uint32_t(ct * BN + 4 * h);
+    bf16x8 db8[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pe = __builtin_amdgcn_exp2f(s[kb][v] * p.scale_log2 - lse2);
+        if (masked) {
+          const uint32_t ko = kbase + uint32_t(kb * 32 + (v >> 2) * 8 + (v & 3));
+          bool vis = false;
+#pragma unroll
+          for (int r = 0; r < MAXR; ++r) vis = vis || (ko - rs[r] < rl[r]);
+          if (!CAUSAL && nr > MAXR) {
+            for (int r = MAXR; r < nr; ++r) {
+              uint2 rr = qvalid ? myruns[r] : make_uint2(0, 0);
+              vis = vis || (ko - rr.x < rr.y - rr.x);
+            }
+          }
+          if (!vis) pe = 0.f;
+        }
+        const float ds = pe * (dp[kb][v] - Dq);
+        db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
+      }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* p1 = sK + kr * LDSTR + db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+        bf16x8 a = cat4(lds_read_tr4(p1), lds_read_tr4(p1 + 8 * LDSTR));
+        acc[db] = mfma32(a, db8[kc], acc[db]);
+      }
+    }
+  }
+
+  if (qvalid) {
+    uint16_t* dQp = p.dq + base + size_t(q) * p.sn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[db][vg * 4 + e] * p.scale);
+        *reinterpret_cast<bf16x4*>(dQp + db * 32 + vg * 8 + 4 * h) = o4;
+      }
+    }
+  }
+}
+
+BwdParams make_params(const AttnDims& a, const DescView& dv) {
+  BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.sb = a.sb; p.sh = a.sh; p.sn = a.sn;
+  p.B = a.B; p.H = a.H; p.N = a.N; p.d = a.d;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  p.Tq_f = (a.N + dv.fq - 1) / dv.fq;
+  p.Tk_f = (a.N + dv.fk - 1) / dv.fk;
+  p.Tk_b = (a.N + dv.bk - 1) / dv.bk;
+  p.Tq_b = (a.N + dv.bq - 1) / dv.bq;
+  p.Wf = dv.Wf; p.fbm = dv.fbm; p.row_iv = reinterpret_cast<const uint2*>(dv.row_iv); p.K_r = dv.K_r;
+  p.row_tkmax = dv.row_tkmax;
+  p.Wb = dv.Wb; p.bbm = dv.bbm; p.col_iv = reinterpret_cast<const uint2*>(dv.col_iv); p.K_c = dv.K_c;
+  p.col_tkmax = dv.col_tkmax;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, float* D, hipStream_t stream) {
+  DescView none;
+  std::memset(&none, 0, sizeof(none));
+  none.fq = none.fk = none.bk = none.bq = 64;
+  BwdParams p = make_params(a, none);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.Dout = D;
+  const int64_t rows = int64_t(a.B) * a.H * a.N;
+  const int rpb = 256 / (a.d / 8);
+  dim3 grid(unsigned((rows + rpb - 1) / rpb));
+  if (a.d == 128) hipLaunchKernelGGL(bwd_dot_kernel<128>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(bwd_dot_kernel<64>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
+                           const void* dO, const float* D, const DescView& dv, void* dk, void* dvv,
+                           hipStream_t stream) {
+  BwdParams p = make_params(a, dv);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.lse = lse;
+  p.D = D;
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dvv);
+  dim3 grid(p.Tk_b, a.H, a.B);
+  const bool c = a.causal != 0;
+#define CM_DKDV(DD, BKK)                                                                              \
+  do {                                                                                               \
+    if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true>), grid, dim3(BKK * 2), 0, stream, p);  \
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false>), grid, dim3(BKK * 2), 0, stream, p);   \
+  } while (0)
+  if (a.d == 128) { if (dv.bk == 128) CM_DKDV(128, 128); else CM_DKDV(128, 64); }
+  else { if (dv.bk == 128) CM_DKDV(64, 128); else CM_DKDV(64, 64); }
+#undef CM_DKDV
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
+                         const void* dO, const float* D, const DescView& dv, void* dq, hipStream_t stream) {
+  BwdParams p = make_params(a, dv);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.lse = lse;
+  p.D = D;
+  p.dq = static_cast<uint16_t*>(dq);
+  dim3 grid(p.Tq_f, a.H, a.B);
+  const bool c = a.causal != 0;
+#define CM_DQ(DD, BMM)                                                                             \
+  do {                                                                                            \
+    if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true>), grid, dim3(BMM * 2), 0, stream, p); \
+    else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false>), grid, dim3(BMM * 2), 0, stream, p);  \
+  } while (0)
+  if (a.d == 128) { if (dv.fq == 128) CM_DQ(128, 128); else CM_DQ(128, 64); }
+  else { if (dv.fq == 128) CM_DQ(64, 128); else CM_DQ(64, 64); }
+#undef CM_DQ
+  return hipGetLastError();
+}
+
+}  // namespace cm

@@ -1,0 +1,89 @@
+// attn_common.h -- CDNA4 (gfx950) building blocks of the attention kernels.
+//
+// Matrix cores: v_mfma_f32_32x32x16_bf16, one wave64.  Operand lane layout
+// (lane l, element e of the 8 bf16 an operand register holds, h = l / 32):
+//   A (32 x 16):  row l % 32, k = 8h + e
+//   B (16 x 32):  col l % 32, k = 8h + e
+//   C (32 x 32):  16 floats, element v at col l % 32, row 8(v/4) + 4h + v%4
+// A contraction may permute k freely as long as A and B agree.  The kernels
+// keep score tiles transposed (keys in the rows of C) so that each lane owns
+// one query row (forward, dQ) or one key column (dK/dV): its interval runs
+// are loop-invariant registers and row statistics need only one exchange with
+// lane l ^ 32.  A score block in C layout feeds the next contraction as a B
+// operand directly when the other operand lists its k in the order
+//   pi(8h + e) = 4h + e (e < 4),  8 + 4h + (e - 4) (e >= 4)
+// within each 16-wide k chunk.
+//
+// ds_read_b64_tr_b16 (gfx950): in each 16-lane group, lane r supplies the
+// address of 4 bf16; lane i receives element i % 4 of the 4-bf16 words of
+// lanes 4e + i / 4, e = 0..3.  Pointing lane r at row kb + r / 4, column
+// nb + 4 (r % 4) of a row-major [k][n] LDS tile gives lane i the column
+// nb + i at rows kb..kb+3: a transposed read, so V, Q, dO and K stay
+// row-major in LDS and still serve as k-major MFMA operands.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cm {
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint4 as_u4(const bf16x8& v) { return __builtin_bit_cast(uint4, v); }
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* p) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+
+// transposed read of 4 bf16 (see header comment)
+__device__ __forceinline__ bf16x4 lds_read_tr4(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat4(const bf16x4& a, const bf16x4& b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Visit the non-empty tiles of one bitmap row (codes 1 full, 2 partial).
+struct TileIter {
+  const uint32_t* words;
+  int W, w;
+  uint32_t word, pending;
+  __device__ void init(const uint32_t* p, int nwords) {
+    words = p; W = nwords; w = -1; word = 0; pending = 0;
+  }
+  // next non-empty tile; false at the end
+  __device__ __forceinline__ bool next(int& tile, int& state) {
+    while (pending == 0) {
+      if (++w >= W) return false;
+      word = uniform(words[w]);
+      pending = (word | (word >> 1)) & 0x55555555u;
+    }
+    const int bit = __builtin_ctz(pending);
+    pending &= pending - 1;
+    tile = w * 16 + bit / 2;
+    state = (word >> bit) & 3;
+    return true;
+  }
+};
+
+}  // namespace attn
+}  // namespace cm

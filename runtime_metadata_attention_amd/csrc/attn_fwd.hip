@@ -1,0 +1,298 @@
+// attn_fwd.hip -- descriptor-guided attention forward (bf16 in, fp32 accumulate).
+//
+// CompileMask paper summary, section 3.3.2 "Descriptor-Guided Attention
+// Execution": the Tile-State Bitmap lets the kernel skip empty tiles, run full
+// tiles without a mask and check visibility only in partial tiles, with
+// unsigned endpoint compares; invisible scores become -inf before the online
+// softmax.  Section 2.1 "Background" describes the tiled kernel this extends.
+//
+// One work-group per (query tile of BM rows, head, sample); BM / 32 waves,
+// each owning 32 query rows.  Scores are computed transposed, S^T = K Q^T, so
+// a lane owns one query row: its visible runs sit in registers for the whole
+// kernel, the partial-tile check is `(j - start) <u (end - start)` per run,
+// and the row max / sum need one exchange with the lane holding the other 16
+// keys of each 32-key block.  Key/value tiles of 64 rows are staged in LDS
+// (row-major, padded); the next tile's global loads are in flight while the
+// current one is computed.  O^T = V^T P^T reads V through transposed LDS
+// reads and takes P^T straight from the score registers.
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+#include "internal.h"
+
+namespace cm {
+namespace {
+
+using namespace attn;
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t sb, sh, sn;
+  int32_t B, H, N;
+  int32_t Tq, Tk;
+  float scale_log2;
+  const uint32_t* fbm;
+  int32_t Wf;
+  const uint2* row_iv;
+  int32_t K_r;
+  const uint32_t* row_tkmax;
+};
+
+constexpr int BN = 64;
+constexpr int MAXR = 4;  // runs kept in registers; more are read from memory
+
+template <int D, int BM, bool CAUSAL>
+__global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
+  constexpr int NW = BM / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LDSTR = D + 8;                 // padded LDS row (bf16 elements)
+  constexpr int CHUNKS = BN * D / 8;           // 16-byte chunks per K (or V) tile
+  constexpr int LPT = CHUNKS / NT;             // chunks per thread
+  static_assert(CHUNKS % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * LDSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * LDSTR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, lq = lane & 31;
+  const int qt = p.Tq - 1 - int(blockIdx.x);  // the longest rows of lower-triangular masks first
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int N = p.N;
+  const int q0 = qt * BM;
+  const int q = q0 + wave * 32 + lq;
+  const bool qvalid = q < N;
+  const size_t base = size_t(b) * p.sb + size_t(head) * p.sh;
+  const uint16_t* Kp = p.k + base;
+  const uint16_t* Vp = p.v + base;
+
+  // Q^T as MFMA B operands: lane holds Q[q][16c + 8h .. +7]
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (qvalid) u = *reinterpret_cast<const uint4*>(p.q + base + size_t(q) * p.sn + 16 * c + 8 * h);
+    qreg[c] = as_bf16x8(u);
+  }
+
+  // this row's visible runs: start and length
+  int nr;
+  uint32_t rs[MAXR], rl[MAXR];
+  const uint2* myruns = nullptr;
+  if (CAUSAL) {
+    nr = 1;
+    rs[0] = 0; rl[0] = uint32_t(q + 1);
+#pragma unroll
+    for (int r = 1; r < MAXR; ++r) { rs[r] = 0; rl[r] = 0; }
+  } else {
+    nr = int(uniform(p.row_tkmax[size_t(b) * p.Tq + qt]));
+    myruns = p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      uint2 v = make_uint2(0, 0);
+      if (r < nr && qvalid) v = myruns[r];
+      rs[r] = v.x;
+      rl[r] = v.y - v.x;
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
+
+  // tile iteration
+  TileIter it;
+  int causal_next = 0, causal_last = 0;
+  if (!CAUSAL) it.init(p.fbm + (size_t(b) * p.Tq + qt) * p.Wf, p.Wf);
+  else causal_last = min(p.Tk - 1, (q0 + BM - 1) / BN);
+  auto next_tile = [&](int& tile, int& state) -> bool {
+    if (CAUSAL) {
+      if (causal_next > causal_last) return false;
+      tile = causal_next++;
+      state = ((tile + 1) * BN - 1 <= q0) ? 1 : 2;
+      return true;
+    }
+    return it.next(tile, state);
+  };
+
+  uint4 pk[LPT], pv[LPT];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int c = tid + NT * j;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int key = tile * BN + row;
+      if (key < N) {
+        pk[j] = *reinterpret_cast<const uint4*>(Kp + size_t(key) * p.sn + col);
+        pv[j] = *reinterpret_cast<const uint4*>(Vp + size_t(key) * p.sn + col);
+      } else {
+        pk[j] = make_uint4(0, 0, 0, 0);
+        pv[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int tile = 0, state = 0;
+  bool have = next_tile(tile, state);
+  if (have) load_tile(tile);
+  const int g = lane >> 4, gi = lane & 15;
+  while (have) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int c = tid + NT * j;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(sK + row * LDSTR + col) = pk[j];
+      *reinterpret_cast<uint4*>(sV + row * LDSTR + col) = pv[j];
+    }
+    __syncthreads();
+    const int ct = tile, cs = state;
+    have = next_tile(tile, state);
+    if (have) load_tile(tile);
+
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 a = lds_read_b128(sK + (kb * 32 + lq) * LDSTR + 16 * c + 8 * h);
+        s[kb] = mfma32(a, qreg[c], s[kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] *= p.scale_log2;
+
+    // partial tiles (and a ragged last tile): unsigned endpoint checks
+    const bool masked = (cs == 2) || ((ct + 1) * BN > N);
+    if (masked) {
+      const uint32_t kbase = uint32_t(ct * BN + 4 * h);
+      uint32_t off[MAXR];
+#pragma unroll
+      for (int r = 0; r < MAXR; ++r) off[r] = kbase - rs[r];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t ko = uint32_t(kb * 32 + (v >> 2) * 8 + (v & 3));
+          bool vis = false;
+#pragma unroll
+          for (int r = 0; r < MAXR; ++r) vis = vis || (off[r] + ko < rl[r]);
+          if (!CAUSAL && nr > MAXR) {
+            for (int r = MAXR; r < nr; ++r) {
+              uint2 rr = qvalid ? myruns[r] : make_uint2(0, 0);
+              vis = vis || (kbase + ko - rr.x < rr.y - rr.x);
+            }
+          }
+          if (!vis) s[kb][v] = -INFINITY;
+        }
+      }
+    }
+
+    // online softmax (log2 domain)
+    float mt = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
+    mt = fmaxf(mt, wave_xor32(mt));
+    const float mn = fmaxf(m, mt);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mu);
+    float rsum = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(s[kc >> 1][(kc & 1) * 8 + e] - mu);
+        rsum += pe;
+        pb[kc][e] = (__bf16)pe;
+      }
+    }
+    lsum = lsum * alpha + rsum;
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* p1 = sV + kr * LDSTR + db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+        bf16x8 a = cat4(lds_read_tr4(p1), lds_read_tr4(p1 + 8 * LDSTR));
+        acc[db] = mfma32(a, pb[kc], acc[db]);
+      }
+    }
+  }
+
+  // epilogue: O = acc / l, lse = ln-sum-exp (natural log)
+  const float lt = lsum + wave_xor32(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qvalid) {
+    uint16_t* Op = p.o + base + size_t(q) * p.sn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[db][vg * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(Op + db * 32 + vg * 8 + 4 * h) = o4;
+      }
+    }
+    if (h == 0) {
+      const float l2 = (m == -INFINITY || lt <= 0.f) ? -INFINITY : (m + __log2f(lt)) * kLn2;
+      p.lse[(size_t(b) * p.H + head) * N + q] = l2;
+    }
+  }
+}
+
+template <int D, int BM, bool CAUSAL>
+hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  dim3 grid(p.Tq, p.H, p.B);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BM, CAUSAL>), grid, dim3(BM * 2), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_tiles_supported(int d, int fq, int fk, int bk, int bq) {
+  (void)d;
+  return (fq == 64 || fq == 128) && fk == 64 && (bk == 64 || bk == 128) && bq == 64;
+}
+
+hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, const void* v, const DescView& dv,
+                           void* o, float* lse, hipStream_t stream) {
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.sb = a.sb; p.sh = a.sh; p.sn = a.sn;
+  p.B = a.B; p.H = a.H; p.N = a.N;
+  p.Tq = (a.N + dv.fq - 1) / dv.fq;
+  p.Tk = (a.N + dv.fk - 1) / dv.fk;
+  p.scale_log2 = a.scale * attn::kLog2e;
+  p.fbm = dv.fbm; p.Wf = dv.Wf; p.row_iv = reinterpret_cast<const uint2*>(dv.row_iv); p.K_r = dv.K_r;
+  p.row_tkmax = dv.row_tkmax;
+  const bool c = a.causal != 0;
+  if (a.d == 128) {
+    if (dv.fq == 128) return c ? launch<128, 128, true>(p, stream) : launch<128, 128, false>(p, stream);
+    return c ? launch<128, 64, true>(p, stream) : launch<128, 64, false>(p, stream);
+  }
+  if (dv.fq == 128) return c ? launch<64, 128, true>(p, stream) : launch<64, 128, false>(p, stream);
+  return c ? launch<64, 64, true>(p, stream) : launch<64, 64, false>(p, stream);
+}
+
+}  // namespace cm

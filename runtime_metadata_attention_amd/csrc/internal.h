@@ -1,0 +1,91 @@
+// internal.h -- host-side types shared by the library's translation units.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/compilemask.h"
+#include "program.h"
+
+struct cm_spec {
+  cm::Program prog;              // lowered endpoint program, both directions
+  int n_words = 0;
+  int dir_off[2] = {2, 2};       // word offset of each direction
+  int fixed_slots[2] = {0, 0};   // largest count of plain slots of a Region
+  // per direction, per region: (plain slots, exists slots); K = max over regions
+  std::vector<std::pair<int, int>> region_slots[2];
+  std::vector<std::string> params;
+  int n_refs = 0;
+  uint64_t id = 0;               // unique per compiled spec
+  std::string listing;           // human-readable lowered program
+};
+
+struct cm_desc {
+  uint64_t spec_id = 0;
+  int32_t B = 0, N = 0, seg_cap = 0, K_r = 0, K_c = 0;
+  cm_tiles tiles{};
+  int32_t Tq_f = 0, Tk_f = 0, Tk_b = 0, Tq_b = 0, Wf = 0, Wb = 0;
+  size_t off[9] = {};            // section offsets + total (same order as cm_desc_offsets)
+  void* buf = nullptr;
+  size_t bytes = 0;
+};
+
+namespace cm {
+
+enum Section { SEC_HEADER = 0, SEC_SAMPLE_ERR, SEC_ROW_TKMAX, SEC_COL_TKMAX, SEC_FBM, SEC_BBM,
+               SEC_ROW_IV, SEC_COL_IV, SEC_TOTAL };
+
+// Thread-local error detail for cm_last_error().
+void set_error(const std::string& msg);
+cm_status fail(cm_status st, const std::string& msg);
+
+// K of a direction for a segment capacity.
+int spec_width(const cm_spec* spec, int dir, int seg_cap);
+
+// Kernel launchers (HIP translation units).
+struct PreprocessArgs {
+  const int32_t* scalars;
+  const int32_t* seg_bounds;
+  const int32_t* n_seg;
+  const int32_t* refs;
+  int32_t n_scalars, n_refs, seg_cap;
+  uint32_t* desc;                 // descriptor base
+  int32_t B, N, K_r, K_c;
+  int32_t fq, fk, bk, bq;         // tile sizes
+  int32_t Tq_f, Tk_f, Tk_b, Tq_b, Wf, Wb;
+  uint32_t off_words[8];          // section offsets in words
+  int32_t dir_off[2];
+};
+hipError_t launch_preprocess(const PreprocessArgs& a, const Program& prog, hipStream_t stream);
+
+struct AttnDims {
+  int32_t B, H, N, d;
+  int64_t sb, sh, sn;            // element strides of the bf16 tensors
+  float scale;
+  int32_t causal;
+};
+struct DescView {                // device pointers into a descriptor
+  const uint32_t* fbm;
+  const uint32_t* bbm;
+  const uint32_t* row_iv;
+  const uint32_t* col_iv;
+  const uint32_t* row_tkmax;
+  const uint32_t* col_tkmax;
+  int32_t K_r, K_c, Wf, Wb, Tq_f, Tk_f, Tk_b, Tq_b;
+  int32_t fq, fk, bk, bq;
+};
+hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, const void* v, const DescView& dv,
+                           void* o, float* lse, hipStream_t stream);
+hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, float* D, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
+                           const void* dO, const float* D, const DescView& dv, void* dk, void* dvv,
+                           hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
+                         const void* dO, const float* D, const DescView& dv, void* dq, hipStream_t stream);
+bool attn_tiles_supported(int d, int fq, int fk, int bk, int bq);
+
+}  // namespace cm

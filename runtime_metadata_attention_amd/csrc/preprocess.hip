@@ -1,0 +1,285 @@
+// preprocess.hip -- online preprocess: batch metadata -> Execution Descriptor.
+//
+// CompileMask paper summary, section 3.3 "Online Efficient Mask Attention
+// Execution": the preprocess kernel evaluates the compiled endpoints against
+// the batch metadata and builds the descriptors of the forward and backward
+// passes; section 3.3.1 "Execution Descriptor": an Interval Table padded with
+// zero-length intervals, and two-bit tile states (empty / full / partial).
+//
+// One launch builds everything.  Grid (Tq_f + Tk_b, B): work-group x < Tq_f
+// owns forward query tile x (its rows' key runs, its forward bitmap row and
+// run maximum); the others own one backward key tile (its columns' row runs,
+// its backward bitmap row and run maximum).  No work-group reads another's
+// output, so there are no global atomics and no memset; every byte of the
+// variable sections is rewritten on every build.
+//
+// Tile states come from two counters per tile of the other axis, kept as
+// difference arrays in LDS: `any` (how many of the work-group's indices have a
+// run touching the tile) and `full` (how many have the whole tile inside one
+// run).  A prefix scan turns them into counts: any == 0 -> empty, full == the
+// number of indices -> full, otherwise partial.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace cm {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Role {
+  int x0, nidx;          // first index and index count of this tile
+  int K;                 // table width
+  uint2* table;          // this sample's interval table
+  int Bt, T, W;          // tile width / count / words along the other axis
+  uint32_t* bitmap;      // this tile's bitmap row
+  uint32_t* tkmax;       // this tile's run maximum
+  int dir_off;
+};
+
+struct Lds {
+  int32_t* any;
+  int32_t* full;
+  int32_t* misc;         // [0] run max, [1] sample error, [2] error OR over samples
+};
+
+__device__ __forceinline__ void count_run(const Lds& L, const Role& r, int N, uint32_t s, uint32_t e) {
+  const int a0 = int(s) / r.Bt, a1 = int(e - 1) / r.Bt;
+  atomicAdd(&L.any[a0], 1);
+  atomicAdd(&L.any[a1 + 1], -1);
+  const int f0 = (int(s) + r.Bt - 1) / r.Bt;
+  const int f1 = (int(e) == N) ? r.T : int(e) / r.Bt;
+  if (f0 < f1) {
+    atomicAdd(&L.full[f0], 1);
+    atomicAdd(&L.full[f1], -1);
+  }
+}
+
+// Runs held in registers: sorted insertion with compile-time indices only.
+template <int KC>
+__device__ __forceinline__ void runs_registers(const Program& prog, const SampleView& sv, const Role& r, const Lds& L, int idx) {
+  uint32_t s[KC], e[KC];
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < KC; ++q) { s[q] = 0; e[q] = 0; }
+  eval_direction(prog.w, r.dir_off, sv, idx, [&](int32_t lo, int32_t hi) {
+    int pos = 0;
+#pragma unroll
+    for (int q = 0; q < KC; ++q) pos += (q < n && s[q] <= uint32_t(lo)) ? 1 : 0;
+#pragma unroll
+    for (int q = KC - 1; q >= 0; --q) {
+      if (q > 0 && q > pos && q <= n) { s[q] = s[q - 1]; e[q] = e[q - 1]; }
+      else if (q == pos) { s[q] = uint32_t(lo); e[q] = uint32_t(hi); }
+    }
+    n = n < KC ? n + 1 : KC;
+  });
+  uint2* row = r.table + size_t(idx) * r.K;
+  int nout = 0;
+  uint32_t cs = 0, ce = 0;
+  bool open = false;
+#pragma unroll
+  for (int q = 0; q < KC; ++q) {
+    if (q < n) {
+      if (open && s[q] <= ce) {
+        ce = e[q] > ce ? e[q] : ce;
+      } else {
+        if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, sv.N, cs, ce); }
+        cs = s[q]; ce = e[q]; open = true;
+      }
+    }
+  }
+  if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, sv.N, cs, ce); }
+  for (int q = nout; q < r.K; ++q) row[q] = make_uint2(0u, 0u);
+  atomicMax(&L.misc[0], nout);
+}
+
+// Wide tables (exists-slots): sort and merge in the index's own table row.
+__device__ __forceinline__ void runs_memory(const Program& prog, const SampleView& sv, const Role& r, const Lds& L, int idx) {
+  uint2* row = r.table + size_t(idx) * r.K;
+  int n = 0;
+  const int K = r.K;
+  eval_direction(prog.w, r.dir_off, sv, idx, [&](int32_t lo, int32_t hi) {
+    if (n >= K) return;
+    int pos = n;
+    while (pos > 0 && row[pos - 1].x > uint32_t(lo)) { row[pos] = row[pos - 1]; --pos; }
+    row[pos] = make_uint2(uint32_t(lo), uint32_t(hi));
+    ++n;
+  });
+  int nout = 0;
+  uint32_t cs = 0, ce = 0;
+  bool open = false;
+  for (int q = 0; q < n; ++q) {
+    const uint2 v = row[q];
+    if (open && v.x <= ce) {
+      ce = v.y > ce ? v.y : ce;
+    } else {
+      if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, sv.N, cs, ce); }
+      cs = v.x; ce = v.y; open = true;
+    }
+  }
+  if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, sv.N, cs, ce); }
+  for (int q = nout; q < K; ++q) row[q] = make_uint2(0u, 0u);
+  atomicMax(&L.misc[0], nout);
+}
+
+// In-place inclusive prefix sums of a[0..T) and b[0..T) by one work-group.
+__device__ void scan2(int32_t* a, int32_t* b, int T, int32_t* part) {
+  const int t = threadIdx.x;
+  const int chunk = (T + kThreads - 1) / kThreads;
+  const int lo = t * chunk, hi = min(T, lo + chunk);
+  int32_t sa = 0, sb = 0;
+  for (int c = lo; c < hi; ++c) { sa += a[c]; sb += b[c]; }
+  part[t] = sa;
+  part[kThreads + t] = sb;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    int32_t va = 0, vb = 0;
+    if (t >= off) { va = part[t - off]; vb = part[kThreads + t - off]; }
+    __syncthreads();
+    part[t] += va;
+    part[kThreads + t] += vb;
+    __syncthreads();
+  }
+  int32_t ra = t > 0 ? part[t - 1] : 0, rb = t > 0 ? part[kThreads + t - 1] : 0;
+  for (int c = lo; c < hi; ++c) {
+    ra += a[c]; a[c] = ra;
+    rb += b[c]; b[c] = rb;
+  }
+  __syncthreads();
+}
+
+// Both structs travel in one kernel argument.  The kernel reads them through
+// the kernarg segment pointer (explicit arguments start at offset 0 of that
+// segment), so that the program, which is indexed with run-time offsets, is
+// read in place with scalar loads instead of being copied to private memory.
+struct KernArgs {
+  PreprocessArgs a;
+  Program prog;
+};
+
+__global__ __launch_bounds__(kThreads) void preprocess_kernel(KernArgs /*in kernarg segment*/) {
+  extern __shared__ int32_t lds[];
+#if defined(__HIP_DEVICE_COMPILE__)
+  const KernArgs* ka = (const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+#else
+  const KernArgs* ka = nullptr;
+#endif
+  const PreprocessArgs& a = ka->a;
+  const Program& prog = ka->prog;
+  const int b = blockIdx.y;
+  const bool row_role = int(blockIdx.x) < a.Tq_f;
+  const int tile = row_role ? int(blockIdx.x) : int(blockIdx.x) - a.Tq_f;
+  uint32_t* desc = a.desc;
+
+  Role r;
+  if (row_role) {
+    r.x0 = tile * a.fq; r.nidx = min(a.fq, a.N - r.x0); r.K = a.K_r;
+    r.table = reinterpret_cast<uint2*>(desc + a.off_words[SEC_ROW_IV]) + size_t(b) * a.N * a.K_r;
+    r.Bt = a.fk; r.T = a.Tk_f; r.W = a.Wf;
+    r.bitmap = desc + a.off_words[SEC_FBM] + (size_t(b) * a.Tq_f + tile) * a.Wf;
+    r.tkmax = desc + a.off_words[SEC_ROW_TKMAX] + size_t(b) * a.Tq_f + tile;
+    r.dir_off = a.dir_off[0];
+  } else {
+    r.x0 = tile * a.bk; r.nidx = min(a.bk, a.N - r.x0); r.K = a.K_c;
+    r.table = reinterpret_cast<uint2*>(desc + a.off_words[SEC_COL_IV]) + size_t(b) * a.N * a.K_c;
+    r.Bt = a.bq; r.T = a.Tq_b; r.W = a.Wb;
+    r.bitmap = desc + a.off_words[SEC_BBM] + (size_t(b) * a.Tk_b + tile) * a.Wb;
+    r.tkmax = desc + a.off_words[SEC_COL_TKMAX] + size_t(b) * a.Tk_b + tile;
+    r.dir_off = a.dir_off[1];
+  }
+
+  // LDS: any[Tmax+1] full[Tmax+1] part[2*threads] misc[4] bounds[seg_cap+1] refs[..] scalars[..]
+  const int Tmax = max(a.Tk_f, a.Tq_b);
+  Lds L;
+  L.any = lds;
+  L.full = lds + (Tmax + 1);
+  int32_t* part = L.full + (Tmax + 1);
+  L.misc = part + 2 * kThreads;
+  int32_t* bounds = L.misc + 4;
+  int32_t* refs = bounds + (a.seg_cap + 1);
+  int32_t* scal = refs + a.seg_cap * a.n_refs;
+
+  const int tid = threadIdx.x;
+  const int n_seg = a.n_seg ? a.n_seg[b] : 0;
+  for (int t = tid; t <= a.seg_cap && a.seg_bounds; t += kThreads) bounds[t] = a.seg_bounds[size_t(b) * (a.seg_cap + 1) + t];
+  for (int t = tid; t < a.seg_cap * a.n_refs; t += kThreads) refs[t] = a.refs[size_t(b) * a.seg_cap * a.n_refs + t];
+  for (int t = tid; t < a.n_scalars; t += kThreads) scal[t] = a.scalars[size_t(b) * a.n_scalars + t];
+  for (int t = tid; t <= r.T; t += kThreads) { L.any[t] = 0; L.full[t] = 0; }
+  if (tid == 0) { L.misc[0] = 0; L.misc[2] = 0; }
+  __syncthreads();
+  if (tid == 0) L.misc[1] = int32_t(validate_sample(a.N, n_seg, a.seg_cap, bounds, refs, a.n_refs));
+  if (blockIdx.x == 0 && b == 0 && tid < a.B) {
+    const int bb = tid;
+    const int ns = a.n_seg ? a.n_seg[bb] : 0;
+    const int32_t* gb = a.seg_bounds ? a.seg_bounds + size_t(bb) * (a.seg_cap + 1) : nullptr;
+    const int32_t* gr = a.refs ? a.refs + size_t(bb) * a.seg_cap * a.n_refs : nullptr;
+    uint32_t e = (ns < 0 || ns > a.seg_cap) ? 1u
+                 : (ns == 0 ? 0u : validate_sample(a.N, ns, a.seg_cap, gb, gr, a.n_refs));
+    atomicOr(reinterpret_cast<uint32_t*>(&L.misc[2]), e);
+  }
+  __syncthreads();
+  const uint32_t err = uint32_t(L.misc[1]);
+
+  SampleView sv;
+  sv.N = a.N;
+  sv.n_seg = n_seg;
+  sv.n_refs = a.n_refs;
+  sv.scalars = scal;
+  sv.bounds = bounds;
+  sv.refs = refs;
+
+  for (int q = tid; q < r.nidx; q += kThreads) {
+    const int idx = r.x0 + q;
+    if (err != 0) {
+      uint2* row = r.table + size_t(idx) * r.K;
+      for (int t = 0; t < r.K; ++t) row[t] = make_uint2(0u, 0u);
+      continue;
+    }
+    if (r.K <= 1) runs_registers<1>(prog, sv, r, L, idx);
+    else if (r.K <= 2) runs_registers<2>(prog, sv, r, L, idx);
+    else if (r.K <= 4) runs_registers<4>(prog, sv, r, L, idx);
+    else if (r.K <= 8) runs_registers<8>(prog, sv, r, L, idx);
+    else runs_memory(prog, sv, r, L, idx);
+  }
+  __syncthreads();
+  scan2(L.any, L.full, r.T, part);
+
+  for (int w = tid; w < r.W; w += kThreads) {
+    uint32_t word = 0;
+    for (int c = 16 * w; c < min(r.T, 16 * w + 16); ++c) {
+      const uint32_t code = L.any[c] == 0 ? 0u : (L.full[c] == r.nidx ? 1u : 2u);
+      word |= code << (2 * (c - 16 * w));
+    }
+    r.bitmap[w] = word;
+  }
+  if (tid == 0) {
+    *r.tkmax = uint32_t(L.misc[0]);
+    if (blockIdx.x == 0) desc[a.off_words[SEC_SAMPLE_ERR] + b] = err;
+    if (blockIdx.x == 0 && b == 0) {
+      uint4* h = reinterpret_cast<uint4*>(desc + a.off_words[SEC_HEADER]);
+      h[0] = make_uint4(CM_DESC_MAGIC, uint32_t(a.B), uint32_t(a.N), uint32_t(a.K_r));
+      h[1] = make_uint4(uint32_t(a.K_c), uint32_t(a.fq), uint32_t(a.fk), uint32_t(a.bk));
+      h[2] = make_uint4(uint32_t(a.bq), uint32_t(a.Tq_f), uint32_t(a.Tk_f), uint32_t(a.Tk_b));
+      h[3] = make_uint4(uint32_t(a.Tq_b), uint32_t(L.misc[2]), uint32_t(a.seg_cap), 0u);
+    }
+  }
+}
+
+}  // namespace
+
+size_t preprocess_lds_bytes(const PreprocessArgs& a) {
+  const int Tmax = a.Tk_f > a.Tq_b ? a.Tk_f : a.Tq_b;
+  return sizeof(int32_t) * (size_t(2) * (Tmax + 1) + 2 * kThreads + 4 + (a.seg_cap + 1) +
+                            size_t(a.seg_cap) * a.n_refs + a.n_scalars);
+}
+
+hipError_t launch_preprocess(const PreprocessArgs& a, const Program& prog, hipStream_t stream) {
+  dim3 grid(a.Tq_f + a.Tk_b, a.B);
+  KernArgs ka;
+  ka.a = a;
+  ka.prog = prog;
+  hipLaunchKernelGGL(preprocess_kernel, grid, dim3(kThreads), preprocess_lds_bytes(a), stream, ka);
+  return hipGetLastError();
+}
+
+}  // namespace cm

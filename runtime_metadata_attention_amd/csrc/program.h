@@ -1,0 +1,222 @@
+// program.h -- encoding and evaluation of a lowered MaskSpec (endpoint program).
+//
+// The symbolic compiler (spec.cpp) lowers each Region's visibility rule to a
+// list of interval slots (CompileMask paper summary, section 3.2.2 "Symbolic
+// Lowering to Visible Intervals").  This header fixes the flat int32 encoding
+// of that result and the routine that evaluates it for one index against one
+// sample's metadata (section 3.3 "Online Efficient Mask Attention Execution":
+// the preprocess kernel evaluates the compiled endpoints).  The same code runs
+// in the preprocess kernel and in the host inspection entry point.
+//
+// Encoding (all int32):
+//   program   : [0] total words, [1] word offset of the backward direction;
+//               the forward direction starts at word 2
+//   direction : n_regions, then the regions
+//   region    : n_guard_atoms | n_slots << 8, guard atoms, slots
+//   slot      : flags (bit 0 = exists-slot) | n_lo << 4 | n_hi << 8 | n_conj << 12,
+//               n_lo terms, n_hi terms, n_conj conjunctions of condition atoms
+//               (each: n_atoms, then the atoms)
+//   atom      : op, term      meaning  term <op> 0, op in {LT, LE, EQ, NE}
+//   term      : base0 | base1 << 16, constant  (value = base0 + base1 + constant)
+//   base (16b): kind (bits 0-2), negate (bit 3), arg (bits 4-15)
+//               SCALAR: arg = scalar index; START/END/SEGID: arg = selector
+//   selector  : root (bit 0: 0 = segment holding the index, 1 = the exists
+//               variable k), hops (bits 1-2), hop ref index h at bits 3+4h
+// A slot's interval is [max(0, lo terms), min(N, hi terms)), empty slots are
+// dropped.  An atom or a bound that names a missing segment (-1, a reference
+// that is absent) is false.  An index uses the first Region whose guard holds;
+// an index in no Region sees nothing.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#include <hip/hip_runtime.h>
+#define CM_HD __host__ __device__ __forceinline__
+#else
+#define CM_HD inline
+#endif
+
+namespace cm {
+
+constexpr int kProgMaxWords = 448;  // kernel-argument budget for both directions
+constexpr int kMaxRegions = 16;
+constexpr int kMaxRefs = 15;
+
+enum BaseKind : int { BK_NONE = 0, BK_IDX = 1, BK_N = 2, BK_SCALAR = 3, BK_START = 4, BK_END = 5, BK_SEGID = 6 };
+enum AtomOp : int { OP_LT = 0, OP_LE = 1, OP_EQ = 2, OP_NE = 3 };
+
+struct Program {
+  int32_t w[kProgMaxWords];
+};
+
+// One sample's metadata as the evaluator sees it.
+struct SampleView {
+  int32_t N;
+  int32_t n_seg;
+  int32_t n_refs;
+  const int32_t* scalars;  // [n_scalars]
+  const int32_t* bounds;   // [n_seg + 1]
+  const int32_t* refs;     // [seg_cap][n_refs]
+};
+
+// Segment holding position x: the last t with bounds[t] <= x, if x < bounds[n_seg].
+CM_HD int segment_of(const SampleView& s, int x) {
+  if (s.n_seg <= 0) return -1;
+  if (x < s.bounds[0] || x >= s.bounds[s.n_seg]) return -1;
+  int lo = 0, hi = s.n_seg;  // invariant: bounds[lo] <= x < bounds[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (s.bounds[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+CM_HD int resolve_selector(const SampleView& s, int sel, int idx_seg, int k) {
+  int g = (sel & 1) ? k : idx_seg;
+  const int hops = (sel >> 1) & 3;
+  for (int h = 0; h < hops; ++h) {
+    if (g < 0 || g >= s.n_seg) return -1;
+    const int r = (sel >> (3 + 4 * h)) & 15;
+    if (r >= s.n_refs) return -1;
+    g = s.refs[g * s.n_refs + r];
+  }
+  return (g >= 0 && g < s.n_seg) ? g : -1;
+}
+
+// Value of one 16-bit base; false when it names a missing segment.
+CM_HD bool eval_base(const SampleView& s, int base, int idx, int idx_seg, int k, int64_t& acc) {
+  const int kind = base & 7;
+  const int arg = (base >> 4) & 0xFFF;
+  int64_t v = 0;
+  switch (kind) {
+    case BK_NONE: return true;
+    case BK_IDX: v = idx; break;
+    case BK_N: v = s.N; break;
+    case BK_SCALAR: v = s.scalars[arg]; break;
+    default: {
+      const int g = resolve_selector(s, arg, idx_seg, k);
+      if (g < 0) return false;
+      v = kind == BK_START ? s.bounds[g] : kind == BK_END ? s.bounds[g + 1] : g;
+    }
+  }
+  acc += (base & 8) ? -v : v;
+  return true;
+}
+
+CM_HD bool eval_term(const SampleView& s, const int32_t* t, int idx, int idx_seg, int k, int64_t& v) {
+  v = t[1];
+  const int b0 = t[0] & 0xFFFF, b1 = (t[0] >> 16) & 0xFFFF;
+  return eval_base(s, b0, idx, idx_seg, k, v) && eval_base(s, b1, idx, idx_seg, k, v);
+}
+
+CM_HD bool eval_atom(const SampleView& s, const int32_t* a, int idx, int idx_seg, int k) {
+  int64_t v;
+  if (!eval_term(s, a + 1, idx, idx_seg, k, v)) return false;
+  switch (a[0]) {
+    case OP_LT: return v < 0;
+    case OP_LE: return v <= 0;
+    case OP_EQ: return v == 0;
+    default: return v != 0;
+  }
+}
+
+constexpr int kAtomWords = 3;
+constexpr int kTermWords = 2;
+
+// Words of a slot starting at p (depends only on program words: uniform).
+CM_HD int slot_words(const int32_t* p) {
+  const int hdr = p[0];
+  const int n_lo = (hdr >> 4) & 15, n_hi = (hdr >> 8) & 15, n_conj = (hdr >> 12) & 15;
+  int w = 1 + kTermWords * (n_lo + n_hi);
+  for (int c = 0; c < n_conj; ++c) w += 1 + kAtomWords * p[w];
+  return w;
+}
+
+// Evaluate a slot for one value of the exists variable k.  Returns true and
+// [lo, hi) when the slot contributes a non-empty interval.
+CM_HD bool eval_slot(const SampleView& s, const int32_t* p, int idx, int idx_seg, int k,
+                     int32_t& lo_out, int32_t& hi_out) {
+  const int hdr = p[0];
+  const int n_lo = (hdr >> 4) & 15, n_hi = (hdr >> 8) & 15, n_conj = (hdr >> 12) & 15;
+  const int32_t* q = p + 1;
+  int64_t lo = 0, hi = s.N;
+  bool ok = true;
+  for (int t = 0; t < n_lo; ++t, q += kTermWords) {
+    int64_t v;
+    ok = ok && eval_term(s, q, idx, idx_seg, k, v);
+    if (ok && v > lo) lo = v;
+  }
+  for (int t = 0; t < n_hi; ++t, q += kTermWords) {
+    int64_t v;
+    ok = ok && eval_term(s, q, idx, idx_seg, k, v);
+    if (ok && v < hi) hi = v;
+  }
+  if (n_conj > 0) {
+    bool any = false;
+    for (int c = 0; c < n_conj; ++c) {
+      const int na = q[0];
+      bool all = true;
+      for (int a = 0; a < na; ++a) all = all && eval_atom(s, q + 1 + kAtomWords * a, idx, idx_seg, k);
+      any = any || all;
+      q += 1 + kAtomWords * na;
+    }
+    ok = ok && any;
+  }
+  if (hi > s.N) hi = s.N;
+  if (lo < 0) lo = 0;
+  lo_out = (int32_t)lo;
+  hi_out = (int32_t)hi;
+  return ok && lo < hi;
+}
+
+// Walk one direction's regions for index idx and hand every non-empty slot
+// interval to emit(lo, hi).  Program words are read at offsets that depend
+// only on the program, so on the GPU every read is wave-uniform.
+template <class Emit>
+CM_HD void eval_direction(const int32_t* prog, int dir_off, const SampleView& s, int idx, Emit&& emit) {
+  const int32_t* p = prog + dir_off;
+  const int n_regions = p[0];
+  ++p;
+  const int idx_seg = segment_of(s, idx);
+  bool matched = false;
+  for (int r = 0; r < n_regions; ++r) {
+    const int n_guard = p[0] & 255, n_slots = (p[0] >> 8) & 255;
+    ++p;
+    bool g = !matched;
+    for (int a = 0; a < n_guard; ++a) g = g && eval_atom(s, p + kAtomWords * a, idx, idx_seg, -1);
+    p += kAtomWords * n_guard;
+    for (int sl = 0; sl < n_slots; ++sl) {
+      if (g) {
+        if (p[0] & 1) {
+          for (int k = 0; k < s.n_seg; ++k) {
+            int32_t lo, hi;
+            if (eval_slot(s, p, idx, idx_seg, k, lo, hi)) emit(lo, hi);
+          }
+        } else {
+          int32_t lo, hi;
+          if (eval_slot(s, p, idx, idx_seg, -1, lo, hi)) emit(lo, hi);
+        }
+      }
+      p += slot_words(p);
+    }
+    matched = matched || g;
+  }
+}
+
+// Metadata validity of one sample (the CM_MD_* bits).
+CM_HD uint32_t validate_sample(int32_t N, int32_t n_seg, int32_t seg_cap, const int32_t* bounds,
+                               const int32_t* refs, int32_t n_refs) {
+  if (n_seg < 0 || n_seg > seg_cap) return 1u;
+  uint32_t err = 0;
+  if (n_seg >= 1) {
+    for (int t = 0; t <= n_seg; ++t) {
+      if (bounds[t] < 0 || bounds[t] > N) err |= 4u;
+      if (t < n_seg && bounds[t + 1] < bounds[t]) err |= 2u;
+    }
+    for (int t = 0; t < n_seg * n_refs; ++t)
+      if (refs[t] < -1 || refs[t] >= n_seg) err |= 8u;
+  }
+  return err;
+}
+
+}  // namespace cm

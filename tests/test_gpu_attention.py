@@ -1,0 +1,197 @@
+"""GPU parity of the attention kernels against the float64 oracle.
+
+O, dQ, dK, dV must match the oracle within max-abs 2e-2 and relative L2 1e-2
+(bf16 inputs, fp32 accumulation); lse within 1e-3 absolute with identical
+-inf positions (rows with no visible key).  The descriptor path and the
+maskless causal path of the same kernels must agree bit for bit on the causal
+mask.  Inputs are the seeded workloads' bf16 tensors; sizes span several tiles
+and end in a ragged tile.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import runtime_metadata_attention_amd as cm
+from runtime_metadata_attention_amd import specs
+from oracle import attention as oa
+from oracle import masks as om
+from tests.test_oracle_masks import small_md
+from workloads import WORKLOADS, make_metadata, make_tensors, metadata_from_segments
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RL2, LSE_ATOL = 2e-2, 1e-2, 1e-3
+
+
+def run_gpu(spec_text, md, t, tiles, causal=False, desc=None, spec=None):
+    """Build the descriptor (unless causal) and run forward + backward."""
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    if not causal:
+        spec = spec or cm.cm_spec_compile(spec_text)
+        desc = desc or cm.Descriptor(spec, B, N, md.seg_cap, tiles)
+        cm.cm_build_descriptor(spec, cm.device_metadata(md), desc)
+    args = cm.attn_args(q, causal=causal)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    cm.cm_attn_fwd(args, q, k, v, None if causal else desc, o, lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device="cuda")
+    cm.cm_attn_bwd(args, q, k, v, o, lse, do, None if causal else desc, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return {n: x.cpu() for n, x in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+
+
+def compare(name, got, want, atol=ATOL, rl2=RL2):
+    g = got.double().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    err = np.abs(g - w)
+    rel = np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30)
+    assert err.max() <= atol and (rel <= rl2 or np.linalg.norm(w) < 1e-6), \
+        f"{name}: max-abs {err.max():.3e} (at {np.unravel_index(err.argmax(), err.shape)}), rel-L2 {rel:.3e}"
+    return err.max(), rel
+
+
+def compare_lse(got, want):
+    g = got.double().numpy()
+    w = np.asarray(want)
+    assert np.array_equal(np.isneginf(g), np.isneginf(w)), "lse: -inf rows differ"
+    fin = np.isfinite(w)
+    if fin.any():
+        assert np.abs(g[fin] - w[fin]).max() <= LSE_ATOL, f"lse: max-abs {np.abs(g[fin] - w[fin]).max():.3e}"
+
+
+def check_all(out, t, mask, md):
+    dq, dk, dv, O, lse = oa.backward(t["q"], t["k"], t["v"], t["do"], om.row_block_fn(mask, md))
+    compare("O", out["o"], O)
+    compare_lse(out["lse"], lse)
+    compare("dq", out["dq"], dq)
+    compare("dk", out["dk"], dk)
+    compare("dv", out["dv"], dv)
+
+
+SMALL = [
+    # mask, N, d, tiles, seed
+    ("causal", 700, 128, (128, 64, 128, 64), 11),
+    ("hstu", 517, 128, (128, 64, 128, 64), 12),
+    ("shared_prompt", 900, 128, (128, 64, 128, 64), 13),
+    ("retrieval", 777, 128, (128, 64, 128, 64), 14),
+    ("shared_prompt", 333, 64, (64, 64, 64, 64), 15),
+    ("retrieval", 450, 64, (128, 64, 64, 64), 16),
+    ("hstu", 300, 128, (64, 64, 128, 64), 17),
+]
+
+
+@pytest.mark.parametrize("mask,N,d,tiles,seed", SMALL)
+def test_small_ragged_parity(mask, N, d, tiles, seed):
+    print(f"[attention] {mask} N={N} d={d} tiles={tiles}", flush=True)
+    md = small_md(mask, N=N, seed=seed, B=2)
+    t = make_tensors(2, 2, N, d, seed)
+    out = run_gpu(specs.BY_MASK[mask], md, t, tiles)
+    check_all(out, t, mask, md)
+
+
+def test_tiny_workload_parity():
+    w = WORKLOADS["shared_prompt_tiny"]
+    md = make_metadata(w)
+    t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
+    out = run_gpu(specs.BY_MASK[w.mask], md, t, w.tiles)
+    check_all(out, t, w.mask, md)
+
+
+def test_empty_rows_give_zero_output_and_no_gradient():
+    # retrieval with no prefix and segments that leave gaps: gap rows see nothing
+    N = 300
+    bounds = [20, 90, 150, 260]
+    md = metadata_from_segments(N, 4, 2, ("g",), [{"scalars": [0], "bounds": bounds, "refs": [[], [0], [0, 1]]}])
+    t = make_tensors(1, 2, N, 128, 21)
+    out = run_gpu(specs.RETRIEVAL, md, t, (128, 64, 128, 64))
+    check_all(out, t, "retrieval", md)
+    empty = np.r_[0:20, 260:300]
+    assert torch.isneginf(out["lse"][0, :, empty]).all()
+    assert (out["o"][0, :, empty].float() == 0).all() and (out["dq"][0, :, empty].float() == 0).all()
+
+
+def test_causal_descriptor_path_equals_maskless_path_bitwise():
+    N = 1000
+    md = small_md("causal", N=N, B=2)
+    t = make_tensors(2, 3, N, 128, 31)
+    a = run_gpu(specs.CAUSAL, md, t, (128, 64, 128, 64))
+    b = run_gpu(None, md, t, None, causal=True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+    check_all(b, t, "causal", md)
+
+
+def test_strided_layout_matches_contiguous():
+    """[B, N, H, d] storage through the stride arguments."""
+    mask, N = "shared_prompt", 400
+    md = small_md(mask, N=N, seed=3, B=2)
+    t = make_tensors(2, 2, N, 128, 41)
+    a = run_gpu(specs.BY_MASK[mask], md, t, (128, 64, 128, 64))
+    ts = {n: x.transpose(1, 2).contiguous().transpose(1, 2) for n, x in t.items()}
+    assert ts["q"].stride()[1] == 128
+    b = run_gpu(specs.BY_MASK[mask], md, ts, (128, 64, 128, 64))
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_forward_bitwise_repeatable_and_desc_reuse():
+    mask, N = "hstu", 640
+    md = small_md(mask, N=N, seed=4, B=2)
+    t = make_tensors(2, 2, N, 128, 51)
+    spec = cm.cm_spec_compile(specs.HSTU)
+    desc = cm.Descriptor(spec, 2, N, md.seg_cap, (128, 64, 128, 64))
+    a = run_gpu(None, md, t, None, desc=desc, spec=spec)
+    b = run_gpu(None, md, t, None, desc=desc, spec=spec)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_argument_errors_launch_nothing():
+    spec = cm.cm_spec_compile(specs.CAUSAL)
+    md = small_md("causal", N=256, B=1)
+    desc = cm.Descriptor(spec, 1, 256, md.seg_cap, (128, 64, 128, 64))
+    q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(q, 7.0)
+    lse = torch.zeros(1, 1, 128, device="cuda")
+    with pytest.raises(cm.CompileMaskError) as e:
+        cm.cm_attn_fwd(cm.attn_args(q), q, q, q, desc, o, lse)      # N mismatch
+    assert e.value.status == -4
+    bad = cm.Descriptor(spec, 1, 128, 0, (64, 32, 128, 64))
+    with pytest.raises(cm.CompileMaskError) as e:
+        cm.cm_attn_fwd(cm.attn_args(q), q, q, q, bad, o, lse)       # no kernel for 64x32 tiles
+    assert e.value.status == -5
+    torch.cuda.synchronize()
+    assert (o == 7.0).all()
+
+
+FULL = ["causal_8k", "hstu_4k", "reward_model_32k", "retrieval4_32k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    """Full workload on the GPU; one (b, h) pair checked on sampled rows and
+    keys against the oracle, which runs that head's whole forward."""
+    w = WORKLOADS[name]
+    md = make_metadata(w)
+    t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
+    print(f"[attention-full] {name}", flush=True)
+    out = run_gpu(specs.BY_MASK[w.mask], md, t, w.tiles)
+    for n in ("o", "dq", "dk", "dv"):
+        assert torch.isfinite(out[n].float()).all(), n
+    b, h = w.B - 1, w.H // 2
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.r_[rng.choice(w.N, 24, replace=False), 0, w.N - 1])
+    keys = np.unique(np.r_[rng.choice(w.N, 24, replace=False), 0, w.N - 1])
+    f = lambda x: oa._f64(x[b, h])  # noqa: E731
+    ref = oa.sampled_head(f(t["q"]), f(t["k"]), f(t["v"]), f(t["do"]), om.row_block_fn(w.mask, md), b, rows, keys,
+                          block=2048)
+    compare("O", out["o"][b, h, rows], ref["O"])
+    compare_lse(out["lse"][b, h, rows], ref["lse"])
+    compare("dq", out["dq"][b, h, rows], ref["dq"])
+    compare("dk", out["dk"][b, h, keys], ref["dk"])
+    compare("dv", out["dv"][b, h, keys], ref["dv"])

@@ -1,0 +1,142 @@
+"""GPU parity of the preprocess kernel: descriptors bit-exact against the oracle.
+
+Every word of the descriptor (header, error words, run maxima, both bitmaps,
+both interval tables and the zero gaps between sections) must equal the CPU
+oracle's, which reads it straight off the dense mask.  Full-size workloads are
+compared through the SHA-256 recorded by tests/golden/make_descriptor_hashes.py
+(the oracle is rebuilt only to report a mismatch); small and edge cases are
+compared with the oracle directly.
+"""
+import hashlib
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import runtime_metadata_attention_amd as cm
+from runtime_metadata_attention_amd import specs
+from oracle import descriptor as od
+from oracle import masks as om
+from tests.test_oracle_masks import small_md
+from workloads import WORKLOADS, make_metadata, metadata_from_segments
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "descriptor_hashes.json")
+
+
+def gpu_descriptor(mask, md, tiles, guard_bytes=0, desc=None, spec=None):
+    spec = spec or cm.cm_spec_compile(specs.BY_MASK[mask])
+    if desc is None:
+        size = cm.cm_desc_size(spec, md.B, md.N, md.seg_cap, tiles)
+        buf = torch.full((size + guard_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+        desc = cm.Descriptor(spec, md.B, md.N, md.seg_cap, tiles, buffer=buf)
+    dmd = cm.device_metadata(md)
+    cm.cm_build_descriptor(spec, dmd, desc)
+    torch.cuda.synchronize()
+    words = desc.buffer[: desc.bytes].cpu().numpy().view(np.uint32)
+    return words, desc, spec
+
+
+def explain(words, want, B, N, K_r, K_c, tiles):
+    g = od.View(words, B, N, K_r, K_c, tiles)
+    o = od.View(want, B, N, K_r, K_c, tiles)
+    bad = []
+    for name in o.shapes:
+        d = np.nonzero(g[name] != o[name])
+        if len(d[0]):
+            bad.append(f"{name}: {len(d[0])} words differ, first at {tuple(int(x[0]) for x in d)}: "
+                       f"got {g[name][tuple(x[0] for x in d)]}, want {o[name][tuple(x[0] for x in d)]}")
+    return "; ".join(bad) or "gaps differ"
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_workloads_bit_exact(name):
+    w = WORKLOADS[name]
+    md = make_metadata(w)
+    gold = json.load(open(GOLDEN))[name]
+    print(f"[descriptor] {name} B={w.B} N={w.N} tiles={w.tiles}", flush=True)
+    words, desc, spec = gpu_descriptor(w.mask, md, w.tiles, guard_bytes=256)
+    assert (desc.K_r, desc.K_c) == (gold["K_r"], gold["K_c"])
+    assert words.nbytes == gold["bytes"]
+    got = hashlib.sha256(words.tobytes()).hexdigest()
+    if got != gold["sha256"]:
+        want = od.build(w.mask, md, desc.K_r, desc.K_c, w.tiles)
+        pytest.fail(explain(words, want, md.B, md.N, desc.K_r, desc.K_c, w.tiles))
+    # nothing written past the end of the descriptor
+    tail = desc.buffer[desc.bytes:].cpu().numpy()
+    assert (tail == 0xA5).all()
+
+
+CASES = [
+    # mask, N, tiles, seed
+    ("causal", 100, (48, 40, 40, 48), 0),
+    ("causal", 777, (128, 64, 128, 64), 1),
+    ("hstu", 513, (64, 64, 64, 64), 2),
+    ("hstu", 1000, (128, 64, 128, 64), 3),
+    ("shared_prompt", 900, (128, 64, 128, 64), 4),
+    ("shared_prompt", 333, (16, 80, 24, 8), 5),
+    ("retrieval", 700, (128, 64, 128, 64), 6),
+    ("retrieval", 451, (32, 32, 96, 16), 7),
+]
+
+
+@pytest.mark.parametrize("mask,N,tiles,seed", CASES)
+def test_small_ragged_cases_bit_exact(mask, N, tiles, seed):
+    md = small_md(mask, N=N, seed=seed, B=3)
+    words, desc, _ = gpu_descriptor(mask, md, tiles, guard_bytes=64)
+    want = od.build(mask, md, desc.K_r, desc.K_c, tiles)
+    assert np.array_equal(words, want), explain(words, want, md.B, N, desc.K_r, desc.K_c, tiles)
+    assert (desc.buffer[desc.bytes:].cpu().numpy() == 0xA5).all()
+
+
+def test_rebuild_reuses_spec_and_overwrites_everything():
+    """Same spec and descriptor, metadata redrawn (HSTU h changes per batch)."""
+    tiles = (128, 64, 128, 64)
+    w = WORKLOADS["hstu_4k"]
+    md1 = make_metadata(w)
+    md2 = make_metadata(w, seed=77)
+    assert not np.array_equal(md1.scalars, md2.scalars)
+    words1, desc, spec = gpu_descriptor("hstu", md1, tiles)
+    words2, _, _ = gpu_descriptor("hstu", md2, tiles, desc=desc, spec=spec)
+    want2 = od.build("hstu", md2, desc.K_r, desc.K_c, tiles)
+    assert np.array_equal(words2, want2), explain(words2, want2, md2.B, md2.N, desc.K_r, desc.K_c, tiles)
+    words1b, _, _ = gpu_descriptor("hstu", md1, tiles, desc=desc, spec=spec)
+    assert np.array_equal(words1b, words1)
+
+
+def test_invalid_metadata_flags_and_empties_the_sample():
+    good = {"scalars": [10], "bounds": [10, 20, 40], "refs": [[-1, -1], [0, -1]]}
+    md = metadata_from_segments(40, 4, 2, ("g",), [good] * 5)
+    md.n_seg[1] = 5
+    md.seg_bounds[2, 1] = 5
+    md.seg_bounds[3, 2] = 41
+    md.refs[4, 1, 0] = 2
+    tiles = (16, 16, 16, 16)
+    # first build with valid metadata everywhere, then the broken batch
+    good_md = metadata_from_segments(40, 4, 2, ("g",), [good] * 5)
+    words, desc, spec = gpu_descriptor("retrieval", good_md, tiles)
+    words, _, _ = gpu_descriptor("retrieval", md, tiles, desc=desc, spec=spec)
+    want = od.build("retrieval", md, desc.K_r, desc.K_c, tiles)
+    assert np.array_equal(words, want), explain(words, want, 5, 40, desc.K_r, desc.K_c, tiles)
+    v = od.View(words, 5, 40, desc.K_r, desc.K_c, tiles)
+    assert v["header"][13] == 15 and v["sample_err"].tolist() == [0, 1, 2, 4, 8]
+
+
+def test_descriptor_bitwise_repeatable():
+    w = WORKLOADS["reward_model_32k"]
+    md = make_metadata(w)
+    a, desc, spec = gpu_descriptor(w.mask, md, w.tiles)
+    b, _, _ = gpu_descriptor(w.mask, md, w.tiles, desc=desc, spec=spec)
+    assert np.array_equal(a, b)
+
+
+def test_mismatched_spec_is_rejected():
+    md = small_md("causal", N=128, B=1)
+    _, desc, _ = gpu_descriptor("causal", md, (64, 64, 64, 64))
+    other = cm.cm_spec_compile(specs.CAUSAL)
+    with pytest.raises(cm.CompileMaskError) as e:
+        cm.cm_build_descriptor(other, cm.device_metadata(md), desc)
+    assert e.value.status == -4
