@@ -1,0 +1,223 @@
+"""Benchmark of the CompileMask hot path on one MI355X.
+
+A step is one pass of the whole path over one batch resident in HBM:
+preprocess (metadata -> Execution Descriptor), attention forward, and the
+three backward kernels (D, dK/dV, dQ).  The metric is visible-pair TFLOP/s of
+forward + backward, 14 * d * V / step time, where V is the exact number of
+visible (query, key) pairs of the batch summed over heads (4 d V forward,
+10 d V backward); the preprocess time is inside the step and reported alone.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line on stdout.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": "attn_fwd.hip",
+    "bwd_dkdv_kernel": "attn_bwd.hip",
+    "bwd_dq_kernel": "attn_bwd.hip",
+    "preprocess_kernel": "preprocess.hip",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    p = os.path.join(ROOT, "runtime_metadata_attention_amd", "csrc", KERNEL_SOURCES[kernel])
+    h = hashlib.sha256()
+    for f in sorted({p, os.path.join(os.path.dirname(p), "attn_common.h")}):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    or None when no measurement matches the kernel's current source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def visible_pairs(desc, H: int) -> int:
+    """V summed over samples and heads, from the descriptor's row runs."""
+    words = desc.words()
+    off = desc.offsets()
+    n = desc.B * desc.N * desc.K_r * 2
+    iv = words[off["row_iv"] // 4: off["row_iv"] // 4 + n].reshape(-1, 2).astype(np.int64)
+    return int((iv[:, 1] - iv[:, 0]).sum()) * H
+
+
+def cpu_baseline(name: str, budget_s: float = 20.0):
+    """The float64 oracle on a bounded sample of the same workload: the
+    forward and backward work of the last query rows of head 0 of sample 0,
+    growing the row block until about `budget_s` of CPU time."""
+    import threadpoolctl
+
+    from oracle import attention as oa
+    from oracle import masks as om
+    from workloads import WORKLOADS, make_metadata, make_tensors
+
+    w = WORKLOADS[name]
+    md = make_metadata(w)
+    t = make_tensors(1, 1, w.N, w.d, w.seed)
+    q, k, v, do = (oa._f64(t[n])[0, 0] for n in ("q", "k", "v", "do"))
+    fn = om.row_block_fn(w.mask, md)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    rows, spent, vis = 64, 0.0, 0
+    while True:
+        r1 = w.N
+        r0 = max(0, r1 - rows)
+        t0 = time.perf_counter()
+        oa.backward_rows(q, k, v, do, fn, 0, r0, r1)
+        spent = time.perf_counter() - t0
+        vis = int(fn(0, r0, r1).sum())
+        if spent > budget_s / 4 or r0 == 0:
+            break
+        rows *= 4
+    tflops = 14.0 * w.d * vis / spent / 1e12
+    return {"value": tflops, "unit": "visible-pair TFLOP/s (fp64 oracle)", "cores": threads, "kind": "oracle",
+            "sample": f"{name}: sample 0, head 0, query rows {r0}..{r1 - 1} ({vis} visible pairs), forward + "
+                      f"backward, {spent:.2f} s", "seconds": spent}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="reward_model_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--causal-path", action="store_true", help="time the maskless causal path (causal masks only)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only: this path has no multi-GPU mode (asked for {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import runtime_metadata_attention_amd as cm
+    from runtime_metadata_attention_amd import specs
+    from workloads import WORKLOADS, make_metadata, make_tensors
+
+    w = WORKLOADS[a.workload]
+    md = make_metadata(w)
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} tiles={w.tiles}")
+    t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
+    del t
+    spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
+    desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev)
+    dmd = cm.device_metadata(md, dev)
+    args = cm.attn_args(q, causal=a.causal_path)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device=dev)
+    use_desc = None if a.causal_path else desc
+
+    names = ["preprocess_kernel", "attn_fwd_kernel", "bwd_dot_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record()
+        mark(0)
+        cm.cm_build_descriptor(spec, dmd, desc)
+        mark(1)
+        cm.cm_attn_fwd(args, q, k, v, use_desc, o, lse)
+        mark(2)
+        for s in range(3):
+            cm.cm_attn_bwd_stage(s, args, q, k, v, o, lse, do, use_desc, dq, dk, dv, ws)
+            mark(3 + s)
+
+    for i in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    V = visible_pairs(desc, w.H)
+    log(f"warmup done; visible pairs V = {V}")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.zeros((a.steps, 5))
+    for i, e in enumerate(evs):
+        for j in range(5):
+            per[i, j] = e[j].elapsed_time(e[j + 1])  # ms
+    avg = per.mean(axis=0)
+    ms_step = wall * 1e3 / a.steps
+    log("per-kernel ms: " + ", ".join(f"{n}={x:.4f}" for n, x in zip(names, avg)))
+
+    d = w.d
+    flops_fb = 14.0 * d * V
+    value = flops_fb / (ms_step * 1e-3) / 1e12
+    # algorithmic flops per launch of each attention kernel (visible pairs only):
+    # forward S and PV (4 d V); dK/dV kernel S, dP, dV, dK (8 d V); dQ kernel S, dP, dQ (6 d V)
+    alg = {"attn_fwd_kernel": 4.0 * d * V, "bwd_dkdv_kernel": 8.0 * d * V, "bwd_dq_kernel": 6.0 * d * V}
+    times = dict(zip(names, avg))
+    dom = max(alg, key=lambda n: times[n])
+    achieved = alg[dom] / (times[dom] * 1e-3) / 1e12
+    traffic = traffic_for(dom, w.name)
+    pre_bytes = desc.bytes + sum(x.numel() * 4 for x in (dmd.scalars, dmd.seg_bounds, dmd.n_seg, dmd.refs)
+                                 if x is not None)
+    line = {
+        "metric": "masked attn fwd+bwd visible-pair TFLOP/s (% bf16 MFMA peak) at 32K; preprocess us",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded metadata and N(0,1) bf16 tensors)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tiles": list(w.tiles),
+                   "seed": w.seed, "visible_pairs": V, "path": "causal" if a.causal_path else "descriptor"},
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "preprocess_us": round(times["preprocess_kernel"] * 1e3, 2),
+        "preprocess_GBps": round(pre_bytes / (times["preprocess_kernel"] * 1e-3) / 1e9, 1),
+        "fwd_tflops": round(4.0 * d * V / (times["attn_fwd_kernel"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(10.0 * d * V / ((times["bwd_dot_kernel"] + times["bwd_dkdv_kernel"] +
+                                             times["bwd_dq_kernel"]) * 1e-3) / 1e12, 2),
+        "kernel_ms": {n: round(float(x), 4) for n, x in times.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cb = cpu_baseline(w.name)
+        line["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()
+                                if k != "seconds"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

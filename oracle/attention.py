@@ -108,6 +108,24 @@ def backward_head(q, k, v, do, mask_rows, b: int, scale=None, block: int = 1024)
     return dq, dk, dv, O, lse
 
 
+def backward_rows(q, k, v, do, mask_rows, b: int, r0: int, r1: int, scale=None):
+    """The work of query rows r0..r1-1 of one (b, h) pair: their forward and
+    their whole share of the backward.  Rows are independent given their own
+    lse and D, so summing dk, dv over a partition of the rows gives
+    backward_head's dk, dv.  Returns dq rows, dk and dv contributions, O rows
+    and lse rows (float64)."""
+    d = q.shape[1]
+    sc = _scale(d, scale)
+    rows = np.arange(r0, r1)
+    O, lse = forward_head(q, k, v, mask_rows, b, rows=rows, scale=scale, block=max(1, r1 - r0))
+    M = mask_rows(b, r0, r1)
+    P = probabilities(q[r0:r1], k, lse, M, scale)
+    Dvec = np.sum(do[r0:r1] * O, axis=1)
+    dP = do[r0:r1] @ v.T
+    dS = P * (dP - Dvec[:, None])
+    return (dS @ k) * sc, (dS.T @ q[r0:r1]) * sc, P.T @ do[r0:r1], O, lse
+
+
 def forward(q, k, v, mask_rows, scale=None, block: int = 1024):
     """All heads: O [B,H,N,d], lse [B,H,N] (float64)."""
     q, k, v = _f64(q), _f64(k), _f64(v)

@@ -148,3 +148,22 @@ def test_sampled_head_equals_full_backward():
     np.testing.assert_allclose(s["dq"], dq[rows], atol=1e-12)
     np.testing.assert_allclose(s["dk"], dk[keys], atol=1e-12)
     np.testing.assert_allclose(s["dv"], dv[keys], atol=1e-12)
+
+
+def test_row_partition_sums_to_full_backward():
+    w = WORKLOADS["shared_prompt_tiny"]
+    md = make_metadata(w)
+    t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
+    q, k, v, do = (oa._f64(t[n])[0, 0] for n in ("q", "k", "v", "do"))
+    fn = om.row_block_fn(w.mask, md)
+    dq, dk, dv, O, lse = oa.backward_head(q, k, v, do, fn, 0)
+    sdk, sdv = np.zeros_like(dk), np.zeros_like(dv)
+    for r0, r1 in [(0, 50), (50, 64), (64, 200), (200, 256)]:
+        pq, pk, pv, pO, pl = oa.backward_rows(q, k, v, do, fn, 0, r0, r1)
+        np.testing.assert_allclose(pq, dq[r0:r1], atol=1e-12)
+        np.testing.assert_allclose(pO, O[r0:r1], atol=1e-13)
+        np.testing.assert_allclose(pl, lse[r0:r1], atol=1e-13)
+        sdk += pk
+        sdv += pv
+    np.testing.assert_allclose(sdk, dk, atol=1e-11)
+    np.testing.assert_allclose(sdv, dv, atol=1e-11)
