@@ -105,7 +105,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, lk = lane & 31;
-  const int kt = p.Tk_b - 1 - int(blockIdx.x);
+  const int kt = int(blockIdx.x);  // first key tiles are seen by the most rows
   const int head = blockIdx.y, b = blockIdx.z;
   const int N = p.N;
   const int k0 = kt * BK;
@@ -226,8 +226,8 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
         dp[qb] = mfma32(ao, vreg[c], dp[qb]);
       }
     }
-    const bool masked = (cs == 2) || ((ct + 1) * BQ > N);
-    const uint32_t qbase = uint32_t(ct * BQ + 4 * h);
+    if ((cs == 2) || ((ct + 1) * BQ > N))
+      mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid);
     bf16x8 pb[4], db8[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -240,20 +240,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = vg * 4 + e;
-          float pe = __builtin_amdgcn_exp2f(s[qb][v] * p.scale_log2 - lv[e]);
-          if (masked) {
-            const uint32_t qo = qbase + uint32_t(qb * 32 + vg * 8 + e);
-            bool vis = false;
-#pragma unroll
-            for (int r = 0; r < MAXR; ++r) vis = vis || (qo - rs[r] < rl[r]);
-            if (!CAUSAL && nr > MAXR) {
-              for (int r = MAXR; r < nr; ++r) {
-                uint2 rr = kvalid ? myruns[r] : make_uint2(0, 0);
-                vis = vis || (qo - rr.x < rr.y - rr.x);
-              }
-            }
-            if (!vis) pe = 0.f;
-          }
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[qb][v], p.scale_log2, -lv[e]));
           const float ds = pe * (dp[qb][v] - dv4[e]);
           const int qc = qb * 2 + (v >> 3), ee = v & 7;
           pb[qc][ee] = (__bf16)pe;
@@ -427,27 +414,14 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
         dp[kb] = mfma32(av, oreg[c], dp[kb]);
       }
     }
-    const bool masked = (cs == 2) || ((ct + 1) * BN > N);
-    const uint32_t kbase = uint32_t(ct * BN + 4 * h);
+    if ((cs == 2) || ((ct + 1) * BN > N))
+      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
     bf16x8 db8[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float pe = __builtin_amdgcn_exp2f(s[kb][v] * p.scale_log2 - lse2);
-        if (masked) {
-          const uint32_t ko = kbase + uint32_t(kb * 32 + (v >> 2) * 8 + (v & 3));
-          bool vis = false;
-#pragma unroll
-          for (int r = 0; r < MAXR; ++r) vis = vis || (ko - rs[r] < rl[r]);
-          if (!CAUSAL && nr > MAXR) {
-            for (int r = MAXR; r < nr; ++r) {
-              uint2 rr = qvalid ? myruns[r] : make_uint2(0, 0);
-              vis = vis || (ko - rr.x < rr.y - rr.x);
-            }
-          }
-          if (!vis) pe = 0.f;
-        }
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
         const float ds = pe * (dp[kb][v] - Dq);
         db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
       }

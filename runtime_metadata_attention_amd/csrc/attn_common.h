@@ -62,6 +62,62 @@ __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 
 
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Offset, inside a 64-wide tile, of element v of 32-block blk of a score
+// tile in C layout, for the lane half h = 0 (add 4h for the other half).
+__device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
+  return uint32_t(blk * 32 + (v >> 2) * 8 + (v & 3));
+}
+
+// Partial-tile visibility (unsigned endpoint compares) for a score tile of two
+// 32-blocks: element e is visible when (base + offset(e) - start_r) <u len_r
+// for some run r; invisible scores become -inf.  `base` is the tile's first
+// index plus 4h.  NR runs are held in registers.
+template <int NR>
+__device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const uint32_t* rs, const uint32_t* rl) {
+  uint32_t off[NR > 0 ? NR : 1];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) off[r] = base - rs[r];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      bool vis = false;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) vis = vis | (off[r] + elem_offset(blk, v) < rl[r]);
+      s[blk][v] = vis ? s[blk][v] : -INFINITY;
+    }
+  }
+}
+
+// Same check with the runs read from memory (rows or columns with more runs
+// than the register copy holds).
+__device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, const uint2* runs, int nr, bool valid) {
+  uint32_t bits = 0;
+  for (int r = 0; r < nr; ++r) {
+    const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
+    const uint32_t off = base - rr.x, len = rr.y - rr.x;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) bits |= uint32_t(off + elem_offset(e >> 4, e & 15) < len) << e;
+  }
+#pragma unroll
+  for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = ((bits >> e) & 1u) ? s[e >> 4][e & 15] : -INFINITY;
+}
+
+// Dispatch on the tile's run maximum (wave-uniform).
+template <int MAXR>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr, const uint32_t* rs,
+                                          const uint32_t* rl, const uint2* runs, bool valid) {
+  static_assert(MAXR == 4, "register copy holds 4 runs");
+  switch (nr) {
+    case 0: mask_runs<0>(s, base, rs, rl); break;
+    case 1: mask_runs<1>(s, base, rs, rl); break;
+    case 2: mask_runs<2>(s, base, rs, rl); break;
+    case 3: mask_runs<3>(s, base, rs, rl); break;
+    case 4: mask_runs<4>(s, base, rs, rl); break;
+    default: mask_runs_mem(s, base, runs, nr, valid); break;
+  }
+}
+
 // Visit the non-empty tiles of one bitmap row (codes 1 full, 2 partial).
 struct TileIter {
   const uint32_t* words;

@@ -163,44 +163,17 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
         s[kb] = mfma32(a, qreg[c], s[kb]);
       }
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] *= p.scale_log2;
-
     // partial tiles (and a ragged last tile): unsigned endpoint checks
-    const bool masked = (cs == 2) || ((ct + 1) * BN > N);
-    if (masked) {
-      const uint32_t kbase = uint32_t(ct * BN + 4 * h);
-      uint32_t off[MAXR];
-#pragma unroll
-      for (int r = 0; r < MAXR; ++r) off[r] = kbase - rs[r];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t ko = uint32_t(kb * 32 + (v >> 2) * 8 + (v & 3));
-          bool vis = false;
-#pragma unroll
-          for (int r = 0; r < MAXR; ++r) vis = vis || (off[r] + ko < rl[r]);
-          if (!CAUSAL && nr > MAXR) {
-            for (int r = MAXR; r < nr; ++r) {
-              uint2 rr = qvalid ? myruns[r] : make_uint2(0, 0);
-              vis = vis || (kbase + ko - rr.x < rr.y - rr.x);
-            }
-          }
-          if (!vis) s[kb][v] = -INFINITY;
-        }
-      }
-    }
+    if ((cs == 2) || ((ct + 1) * BN > N))
+      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
 
-    // online softmax (log2 domain)
+    // online softmax in the log2 domain; the scale is folded into the exponent
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
-    mt = fmaxf(mt, wave_xor32(mt));
+    mt = fmaxf(mt, wave_xor32(mt)) * p.scale_log2;
     const float mn = fmaxf(m, mt);
     const float mu = (mn == -INFINITY) ? 0.f : mn;
     const float alpha = __builtin_amdgcn_exp2f(m - mu);
@@ -210,7 +183,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(s[kc >> 1][(kc & 1) * 8 + e] - mu);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][(kc & 1) * 8 + e], p.scale_log2, -mu));
         rsum += pe;
         pb[kc][e] = (__bf16)pe;
       }
