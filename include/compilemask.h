@@ -193,7 +193,8 @@ cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_des
 cm_status cm_attn_fwd(const cm_attn_args* args, const void* q, const void* k, const void* v,
                       const cm_desc* desc, void* o, float* lse, cm_stream stream);
 
-/* Bytes of fp32 workspace cm_attn_bwd needs (rowsum(dO * O) per row). */
+/* Bytes of fp32 workspace cm_attn_bwd needs: per row, rowsum(dO * O) and
+ * the row's lse in log2 units (2 * B * H * N floats). */
 cm_status cm_attn_bwd_workspace(const cm_attn_args* args, size_t* bytes);
 
 /* Backward from the forward's o and lse: dq, dk, dv (bf16).  Three kernels on

@@ -60,6 +60,12 @@ def build(jobs: int = 8, debug: bool = False, extra=None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host-side launch stub was not emitted leaves an undefined
+    # symbol that would only surface when the library is loaded
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the library: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

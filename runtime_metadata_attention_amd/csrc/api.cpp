@@ -301,7 +301,7 @@ cm_status cm_attn_fwd(const cm_attn_args* args, const void* q, const void* k, co
 cm_status cm_attn_bwd_workspace(const cm_attn_args* args, size_t* bytes) {
   if (!args || !bytes) return fail(CM_ERR_NULL, "args and bytes are required");
   if (args->B < 1 || args->H < 1 || args->N < 1) return fail(CM_ERR_INVALID, "B, H, N must be >= 1");
-  *bytes = size_t(args->B) * args->H * args->N * sizeof(float);
+  *bytes = 2 * size_t(args->B) * args->H * args->N * sizeof(float);
   return CM_OK;
 }
 
@@ -324,7 +324,7 @@ cm_status cm_attn_bwd_stage(int32_t stage, const cm_attn_args* args, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* D = static_cast<float*>(workspace);
   hipError_t e = hipSuccess;
-  if (stage == -1 || stage == 0) e = launch_bwd_dot(dims, o, dO, D, s);
+  if (stage == -1 || stage == 0) e = launch_bwd_dot(dims, o, dO, lse, D, s);
   if (e == hipSuccess && (stage == -1 || stage == 1)) e = launch_bwd_dkdv(dims, q, k, v, lse, dO, D, view, dk, dv, s);
   if (e == hipSuccess && (stage == -1 || stage == 2)) e = launch_bwd_dq(dims, q, k, v, lse, dO, D, view, dq, s);
   if (e != hipSuccess) return hip_fail(e, "cm_attn_bwd");

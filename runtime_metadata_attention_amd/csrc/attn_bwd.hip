@@ -38,11 +38,13 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* dO;
   const float* lse;
-  const float* D;
+  const float* D;        // rowsum(dO * O), [B][H][N]
+  const float* lse2;     // lse * log2(e), +inf for rows with no visible key, [B][H][N]
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
   float* Dout;
+  float* lse2out;
   int64_t sb, sh, sn;
   int32_t B, H, N, d;
   float scale, scale_log2;
@@ -86,22 +88,24 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int s = LPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < total && (t % LPR) == 0) p.Dout[row] = acc;
+  if (row < total && (t % LPR) == 0) {
+    p.Dout[row] = acc;
+    const float x = p.lse[row];
+    p.lse2out[row] = (x == -INFINITY) ? INFINITY : x * kLog2e;
+  }
 }
 
 // ------------------------------------------------------------------ dK / dV
 
 template <int D, int BK, bool CAUSAL>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NT = BK * 2;
-  constexpr int LDSTR = D + 8;
-  constexpr int CHUNKS = BQ * D / 8;
-  constexpr int LPT = CHUNKS / NT;
-  static_assert(CHUNKS % NT == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * LDSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[BQ * LDSTR];  // dO tile
-  __shared__ __attribute__((aligned(16))) float sL[BQ];             // lse * log2(e); +inf = no row
-  __shared__ __attribute__((aligned(16))) float sD[BQ];
+  constexpr int NW = BK / 32;
+  static_assert(NW >= 2, "two waves copy lse2 and D");
+  // Q and dO tiles (double-buffered, swizzled) and the tile's lse2 / D rows
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BQ * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sO[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, lk = lane & 31;
@@ -112,10 +116,22 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int key = k0 + wave * 32 + lk;
   const bool kvalid = key < N;
   const size_t base = size_t(b) * p.sb + size_t(head) * p.sh;
-  const uint16_t* Qp = p.q + base;
-  const uint16_t* Op = p.dO + base;
   const size_t rbase = (size_t(b) * p.H + head) * N;
+  const __amdgpu_buffer_rsrc_t rQ = slice_rsrc(p.q + base, N, p.sn, D);
+  const __amdgpu_buffer_rsrc_t rO = slice_rsrc(p.dO + base, N, p.sn, D);
+  const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.lse2 + rbase), 0, N * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rDv = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.D + rbase), 0, N * 4, 0x00020000);
+  TileDma<D, BQ, NW> dma;
+  dma.init(wave, lane, p.sn);
+  const uint32_t tile_bytes = uint32_t(BQ * p.sn * 2);
+  auto issue = [&](int tile, int bf) {
+    dma.issue(rQ, sQ[bf], uint32_t(tile) * tile_bytes);
+    dma.issue(rO, sO[bf], uint32_t(tile) * tile_bytes);
+    if (wave == 0) dma_row_floats(rL, sL[bf], lane, uint32_t(tile * BQ * 4));
+    else if (wave == 1) dma_row_floats(rDv, sD[bf], lane, uint32_t(tile * BQ * 4));
+  };
 
+  // this wave's keys as B operands: K[key][16c + 8h ..], V[key][16c + 8h ..]
   bf16x8 kreg[D / 16], vreg[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
@@ -128,6 +144,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     vreg[c] = as_bf16x8(uv);
   }
 
+  // this key column's visible query-row runs
   int nr;
   uint32_t rs[MAXR], rl[MAXR];
   const uint2* myruns = nullptr;
@@ -166,75 +183,58 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     return it.next(tile, state);
   };
 
-  uint4 pq[LPT], po[LPT];
-  float pl = 0.f, pd = 0.f;
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int c = tid + NT * j;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int qi = tile * BQ + row;
-      if (qi < N) {
-        pq[j] = *reinterpret_cast<const uint4*>(Qp + size_t(qi) * p.sn + col);
-        po[j] = *reinterpret_cast<const uint4*>(Op + size_t(qi) * p.sn + col);
-      } else {
-        pq[j] = make_uint4(0, 0, 0, 0);
-        po[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (tid < BQ) {
-      const int qi = tile * BQ + tid;
-      float l = INFINITY, dd = 0.f;
-      if (qi < N) {
-        const float x = p.lse[rbase + qi];
-        l = (x == -INFINITY) ? INFINITY : x * kLog2e;
-        dd = p.D[rbase + qi];
-      }
-      pl = l;
-      pd = dd;
-    }
-  };
-
-  int tile = 0, state = 0;
+  int tile = 0, state = 0, buf = 0;
   bool have = next_tile(tile, state);
-  if (have) load_tile(tile);
+  if (have) issue(tile, 0);
   const int g = lane >> 4, gi = lane & 15;
   while (have) {
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int c = tid + NT * j;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(sQ + row * LDSTR + col) = pq[j];
-      *reinterpret_cast<uint4*>(sO + row * LDSTR + col) = po[j];
-    }
-    if (tid < BQ) { sL[tid] = pl; sD[tid] = pd; }
-    __syncthreads();
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
-    if (have) load_tile(tile);
+    wait_vmem();
+    __syncthreads();
+    if (have) issue(tile, buf ^ 1);
+    const uint16_t* cQ = sQ[buf];
+    const uint16_t* cO = sO[buf];
 
     // S = Q K^T and dP = dO V^T: two 32-row blocks, lane = key column
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    {
+      bf16x8 qa[D / 8], oa[D / 8];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+      for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        bf16x8 aq = lds_read_b128(sQ + (qb * 32 + lk) * LDSTR + 16 * c + 8 * h);
-        s[qb] = mfma32(aq, kreg[c], s[qb]);
-        bf16x8 ao = lds_read_b128(sO + (qb * 32 + lk) * LDSTR + 16 * c + 8 * h);
-        dp[qb] = mfma32(ao, vreg[c], dp[qb]);
+        for (int qb = 0; qb < 2; ++qb) qa[2 * c + qb] = lds_read_b128(cQ + swz<D>(qb * 32 + lk, 16 * c + 8 * h));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) oa[2 * c + qb] = lds_read_b128(cO + swz<D>(qb * 32 + lk, 16 * c + 8 * h));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) s[qb] = mfma32(qa[2 * c + qb], kreg[c], s[qb]);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma32(oa[2 * c + qb], vreg[c], dp[qb]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 8, 0);
     }
     if ((cs == 2) || ((ct + 1) * BQ > N))
       mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid);
     bf16x8 pb[4], db8[4];
+    const float* cL = sL[buf];
+    const float* cD = sD[buf];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
-        const float4 l4 = *reinterpret_cast<const float4*>(sL + qb * 32 + vg * 8 + 4 * h);
-        const float4 d4 = *reinterpret_cast<const float4*>(sD + qb * 32 + vg * 8 + 4 * h);
+        const float4 l4 = *reinterpret_cast<const float4*>(cL + qb * 32 + vg * 8 + 4 * h);
+        const float4 d4 = *reinterpret_cast<const float4*>(cD + qb * 32 + vg * 8 + 4 * h);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -249,20 +249,43 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
     // dV^T += dO^T P ; dK^T += Q^T dS   (k = query, in the score-register order)
+    {
+      bf16x8 ot[4 * (D / 32)], qt[4 * (D / 32)];
 #pragma unroll
-    for (int qc = 0; qc < 4; ++qc) {
-      const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
+      for (int qc = 0; qc < 4; ++qc) {
+        const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
 #pragma unroll
-      for (int dbk = 0; dbk < D / 32; ++dbk) {
-        const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
-        const uint16_t* po1 = sO + kr * LDSTR + col;
-        bf16x8 ao = cat4(lds_read_tr4(po1), lds_read_tr4(po1 + 8 * LDSTR));
-        adv[dbk] = mfma32(ao, pb[qc], adv[dbk]);
-        const uint16_t* pq1 = sQ + kr * LDSTR + col;
-        bf16x8 aq = cat4(lds_read_tr4(pq1), lds_read_tr4(pq1 + 8 * LDSTR));
-        adk[dbk] = mfma32(aq, db8[qc], adk[dbk]);
+        for (int dbk = 0; dbk < D / 32; ++dbk) {
+          const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
+          ot[qc * (D / 32) + dbk] = cat4(lds_read_tr4(cO + swz<D>(kr, col)), lds_read_tr4(cO + swz<D>(kr + 8, col)));
+        }
       }
+#pragma unroll
+      for (int qc = 0; qc < 4; ++qc) {
+        const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
+#pragma unroll
+        for (int dbk = 0; dbk < D / 32; ++dbk) {
+          const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
+          qt[qc * (D / 32) + dbk] = cat4(lds_read_tr4(cQ + swz<D>(kr, col)), lds_read_tr4(cQ + swz<D>(kr + 8, col)));
+        }
+      }
+#pragma unroll
+      for (int qc = 0; qc < 4; ++qc)
+#pragma unroll
+        for (int dbk = 0; dbk < D / 32; ++dbk) adv[dbk] = mfma32(ot[qc * (D / 32) + dbk], pb[qc], adv[dbk]);
+#pragma unroll
+      for (int qc = 0; qc < 4; ++qc)
+#pragma unroll
+        for (int dbk = 0; dbk < D / 32; ++dbk) adk[dbk] = mfma32(qt[qc * (D / 32) + dbk], db8[qc], adk[dbk]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (D / 32), 0);
+#pragma unroll
+      for (int i = 0; i < 4 * (D / 32); ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * (D / 32), 0);
     }
+    buf ^= 1;
   }
 
   if (kvalid) {
@@ -290,13 +313,8 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 template <int D, int BM, bool CAUSAL>
 __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BM / 32;
-  constexpr int NT = NW * 64;
-  constexpr int LDSTR = D + 8;
-  constexpr int CHUNKS = BN * D / 8;
-  constexpr int LPT = CHUNKS / NT;
-  static_assert(CHUNKS % NT == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * LDSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * LDSTR];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, lq = lane & 31;
@@ -307,9 +325,12 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   const int q = q0 + wave * 32 + lq;
   const bool qvalid = q < N;
   const size_t base = size_t(b) * p.sb + size_t(head) * p.sh;
-  const uint16_t* Kp = p.k + base;
-  const uint16_t* Vp = p.v + base;
   const size_t rbase = (size_t(b) * p.H + head) * N;
+  const __amdgpu_buffer_rsrc_t rK = slice_rsrc(p.k + base, N, p.sn, D);
+  const __amdgpu_buffer_rsrc_t rV = slice_rsrc(p.v + base, N, p.sn, D);
+  TileDma<D, BN, NW> dma;
+  dma.init(wave, lane, p.sn);
+  const uint32_t tile_bytes = uint32_t(BN * p.sn * 2);
 
   bf16x8 qreg[D / 16], oreg[D / 16];
 #pragma unroll
@@ -322,12 +343,8 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
     qreg[c] = as_bf16x8(uq);
     oreg[c] = as_bf16x8(uo);
   }
-  float lse2 = INFINITY, Dq = 0.f;
-  if (qvalid) {
-    const float x = p.lse[rbase + q];
-    lse2 = (x == -INFINITY) ? INFINITY : x * kLog2e;
-    Dq = p.D[rbase + q];
-  }
+  const float lse2 = qvalid ? p.lse2[rbase + q] : INFINITY;
+  const float Dq = qvalid ? p.D[rbase + q] : 0.f;
 
   int nr;
   uint32_t rs[MAXR], rl[MAXR];
@@ -367,52 +384,52 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
     return it.next(tile, state);
   };
 
-  uint4 pk[LPT], pv[LPT];
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int c = tid + NT * j;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kk = tile * BN + row;
-      if (kk < N) {
-        pk[j] = *reinterpret_cast<const uint4*>(Kp + size_t(kk) * p.sn + col);
-        pv[j] = *reinterpret_cast<const uint4*>(Vp + size_t(kk) * p.sn + col);
-      } else {
-        pk[j] = make_uint4(0, 0, 0, 0);
-        pv[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  int tile = 0, state = 0;
+  int tile = 0, state = 0, buf = 0;
   bool have = next_tile(tile, state);
-  if (have) load_tile(tile);
+  if (have) {
+    dma.issue(rK, sK[0], uint32_t(tile) * tile_bytes);
+    dma.issue(rV, sV[0], uint32_t(tile) * tile_bytes);
+  }
   const int g = lane >> 4, gi = lane & 15;
   while (have) {
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int c = tid + NT * j;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(sK + row * LDSTR + col) = pk[j];
-      *reinterpret_cast<uint4*>(sV + row * LDSTR + col) = pv[j];
-    }
-    __syncthreads();
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
-    if (have) load_tile(tile);
+    wait_vmem();
+    __syncthreads();
+    if (have) {
+      dma.issue(rK, sK[buf ^ 1], uint32_t(tile) * tile_bytes);
+      dma.issue(rV, sV[buf ^ 1], uint32_t(tile) * tile_bytes);
+    }
+    const uint16_t* cK = sK[buf];
+    const uint16_t* cV = sV[buf];
 
     // S^T = K Q^T and dP^T = V dO^T (lane = query)
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    {
+      bf16x8 ka[D / 8], va[D / 8];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+      for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 ak = lds_read_b128(sK + (kb * 32 + lq) * LDSTR + 16 * c + 8 * h);
-        s[kb] = mfma32(ak, qreg[c], s[kb]);
-        bf16x8 av = lds_read_b128(sV + (kb * 32 + lq) * LDSTR + 16 * c + 8 * h);
-        dp[kb] = mfma32(av, oreg[c], dp[kb]);
+        for (int kb = 0; kb < 2; ++kb) ka[2 * c + kb] = lds_read_b128(cK + swz<D>(kb * 32 + lq, 16 * c + 8 * h));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) va[2 * c + kb] = lds_read_b128(cV + swz<D>(kb * 32 + lq, 16 * c + 8 * h));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[2 * c + kb], qreg[c], s[kb]);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(va[2 * c + kb], oreg[c], dp[kb]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 8, 0);
     }
     if ((cs == 2) || ((ct + 1) * BN > N))
       mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
@@ -426,17 +443,26 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
         db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
       }
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T (K read transposed from LDS)
+    {
+      bf16x8 kt[4 * (D / 32)];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
+      for (int kc = 0; kc < 4; ++kc) {
+        const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* p1 = sK + kr * LDSTR + db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-        bf16x8 a = cat4(lds_read_tr4(p1), lds_read_tr4(p1 + 8 * LDSTR));
-        acc[db] = mfma32(a, db8[kc], acc[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+          kt[kc * (D / 32) + db] = cat4(lds_read_tr4(cK + swz<D>(kr, col)), lds_read_tr4(cK + swz<D>(kr + 8, col)));
+        }
       }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(kt[kc * (D / 32) + db], db8[kc], acc[db]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * (D / 32), 0);
     }
+    buf ^= 1;
   }
 
   if (qvalid) {
@@ -474,7 +500,8 @@ BwdParams make_params(const AttnDims& a, const DescView& dv) {
 
 }  // namespace
 
-hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, float* D, hipStream_t stream) {
+hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, const float* lse, float* D,
+                          hipStream_t stream) {
   DescView none;
   std::memset(&none, 0, sizeof(none));
   none.fq = none.fk = none.bk = none.bq = 64;
@@ -482,6 +509,8 @@ hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, floa
   p.o = static_cast<const uint16_t*>(o);
   p.dO = static_cast<const uint16_t*>(dO);
   p.Dout = D;
+  p.lse = lse;
+  p.lse2out = D + size_t(a.B) * a.H * a.N;
   const int64_t rows = int64_t(a.B) * a.H * a.N;
   const int rpb = 256 / (a.d / 8);
   dim3 grid(unsigned((rows + rpb - 1) / rpb));
@@ -500,6 +529,7 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
   p.dO = static_cast<const uint16_t*>(dO);
   p.lse = lse;
   p.D = D;
+  p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dvv);
   dim3 grid(p.Tk_b, a.H, a.B);
@@ -524,6 +554,7 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
   p.dO = static_cast<const uint16_t*>(dO);
   p.lse = lse;
   p.D = D;
+  p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dq = static_cast<uint16_t*>(dq);
   dim3 grid(p.Tq_f, a.H, a.B);
   const bool c = a.causal != 0;

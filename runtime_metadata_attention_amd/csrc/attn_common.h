@@ -62,6 +62,78 @@ __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 
 
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Swizzled row-major LDS tile of D bf16 columns (no padding).  The 16-byte
+// chunk c of row r lives at chunk c ^ f(r).  f makes both access patterns the
+// kernels use conflict-free on 64 four-byte banks: 16 consecutive rows read at
+// one chunk (MFMA operand rows, ds_read_b128), and 4 consecutive rows (from a
+// multiple of 4) read across 4 consecutive chunks (ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int swz_f(int row) {
+  static_assert(D == 64 || D == 128, "head dim");
+  return (D == 128) ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz_f<D>(row)) << 3) | (col & 7));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Buffer resource over one (sample, head) slice of a [.., N, stride_n] bf16
+// tensor: rows at or past N read as zero (hardware range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* base, int N, int64_t sn, int D) {
+  const uint32_t bytes = uint32_t(((int64_t(N) - 1) * sn + D) * 2);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// Asynchronous copy of a BR x D bf16 tile from global memory straight into a
+// swizzled LDS tile (buffer_load ... lds, 16 bytes per lane).  Each wave
+// instruction fills 1 KiB of LDS contiguously (lane l at +16 l), so every lane
+// fetches the global chunk that belongs at its LDS slot.  The NW waves of the
+// work-group share the tile.  Completion: s_waitcnt vmcnt + a barrier.
+template <int D, int BR, int NW>
+struct TileDma {
+  static constexpr int BLOCKS = BR * D * 2 / 1024;
+  static constexpr int PER_WAVE = BLOCKS / NW;
+  static_assert(BLOCKS % NW == 0, "tile split");
+  uint32_t voff[PER_WAVE];
+  int wave;
+  __device__ void init(int wave_, int lane, int64_t sn) {
+    wave = wave_;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int p = (wave * PER_WAVE + j) * 512 + lane * 8;  // element index in the LDS tile
+      const int row = p / D, pc = (p % D) >> 3;
+      const int lc = pc ^ swz_f<D>(row);
+      voff[j] = uint32_t((int64_t(row) * sn + lc * 8) * 2);
+    }
+  }
+  // row0_bytes: byte offset of the tile's first row in the slice (wave-uniform)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint16_t* lds_tile, uint32_t row0_bytes) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds_tile + (wave * PER_WAVE + j) * 512), 16, voff[j],
+                                               row0_bytes, 0, 0);
+#endif
+  }
+};
+
+// One wave copies 64 consecutive floats (starting `first_bytes` into the
+// buffer) straight into LDS.  (The LDS-copy builtins exist only in the device
+// pass; the host pass, which only needs the kernels' launch stubs, skips them.)
+__device__ __forceinline__ void dma_row_floats(__amdgpu_buffer_rsrc_t rs, float* lds, int lane, uint32_t first_bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 4, uint32_t(lane * 4), first_bytes, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Scheduling-group masks (AMDGPU sched_group_barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 // Offset, inside a 64-wide tile, of element v of 32-block blk of a score
 // tile in C layout, for the lane half h = 0 (add 4h for the other half).
 __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {

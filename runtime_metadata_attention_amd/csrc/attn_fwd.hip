@@ -48,13 +48,9 @@ constexpr int MAXR = 4;  // runs kept in registers; more are read from memory
 template <int D, int BM, bool CAUSAL>
 __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int NW = BM / 32;
-  constexpr int NT = NW * 64;
-  constexpr int LDSTR = D + 8;                 // padded LDS row (bf16 elements)
-  constexpr int CHUNKS = BN * D / 8;           // 16-byte chunks per K (or V) tile
-  constexpr int LPT = CHUNKS / NT;             // chunks per thread
-  static_assert(CHUNKS % NT == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * LDSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * LDSTR];
+  // K and V tiles, double-buffered, swizzled (see swz())
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, lq = lane & 31;
@@ -65,8 +61,11 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   const int q = q0 + wave * 32 + lq;
   const bool qvalid = q < N;
   const size_t base = size_t(b) * p.sb + size_t(head) * p.sh;
-  const uint16_t* Kp = p.k + base;
-  const uint16_t* Vp = p.v + base;
+  const __amdgpu_buffer_rsrc_t rK = slice_rsrc(p.k + base, N, p.sn, D);
+  const __amdgpu_buffer_rsrc_t rV = slice_rsrc(p.v + base, N, p.sn, D);
+  TileDma<D, BN, NW> dma;
+  dma.init(wave, lane, p.sn);
+  const uint32_t tile_bytes = uint32_t(BN * p.sn * 2);
 
   // Q^T as MFMA B operands: lane holds Q[q][16c + 8h .. +7]
   bf16x8 qreg[D / 16];
@@ -118,65 +117,65 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     return it.next(tile, state);
   };
 
-  uint4 pk[LPT], pv[LPT];
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int c = tid + NT * j;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = tile * BN + row;
-      if (key < N) {
-        pk[j] = *reinterpret_cast<const uint4*>(Kp + size_t(key) * p.sn + col);
-        pv[j] = *reinterpret_cast<const uint4*>(Vp + size_t(key) * p.sn + col);
-      } else {
-        pk[j] = make_uint4(0, 0, 0, 0);
-        pv[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  int tile = 0, state = 0;
+  int tile = 0, state = 0, buf = 0;
   bool have = next_tile(tile, state);
-  if (have) load_tile(tile);
+  if (have) {
+    dma.issue(rK, sK[0], uint32_t(tile) * tile_bytes);
+    dma.issue(rV, sV[0], uint32_t(tile) * tile_bytes);
+  }
   const int g = lane >> 4, gi = lane & 15;
   while (have) {
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int c = tid + NT * j;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(sK + row * LDSTR + col) = pk[j];
-      *reinterpret_cast<uint4*>(sV + row * LDSTR + col) = pv[j];
-    }
-    __syncthreads();
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
-    if (have) load_tile(tile);
+    wait_vmem();       // this tile's copies have landed
+    __syncthreads();   // ... for every wave; and nobody still reads the other buffer
+    if (have) {
+      dma.issue(rK, sK[buf ^ 1], uint32_t(tile) * tile_bytes);
+      dma.issue(rV, sV[buf ^ 1], uint32_t(tile) * tile_bytes);
+    }
+    const uint16_t* cK = sK[buf];
+    const uint16_t* cV = sV[buf];
 
-    // S^T = K Q^T for two 32-key blocks
+    // S^T = K Q^T for two 32-key blocks: all operand reads first, then the MFMAs
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      bf16x8 ka[D / 8];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+      for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 a = lds_read_b128(sK + (kb * 32 + lq) * LDSTR + 16 * c + 8 * h);
-        s[kb] = mfma32(a, qreg[c], s[kb]);
-      }
+        for (int kb = 0; kb < 2; ++kb) ka[2 * c + kb] = lds_read_b128(cK + swz<D>(kb * 32 + lq, 16 * c + 8 * h));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[2 * c + kb], qreg[c], s[kb]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 8, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 8, 0);
     }
     // partial tiles (and a ragged last tile): unsigned endpoint checks
     if ((cs == 2) || ((ct + 1) * BN > N))
       mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
 
-    // online softmax in the log2 domain; the scale is folded into the exponent
+    // online softmax in the log2 domain, scale folded into the exponent.  The
+    // running max is only moved (and O rescaled) when some row's max grew by
+    // more than 2^8; otherwise probabilities up to 256 are accumulated against
+    // the stale max, which leaves O = acc / l unchanged.
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
     mt = fmaxf(mt, wave_xor32(mt)) * p.scale_log2;
-    const float mn = fmaxf(m, mt);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - mu);
+    if (__any(mt > m + 8.f)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.f : mn));
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+      m = mn;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
     float rsum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -188,24 +187,28 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
         pb[kc][e] = (__bf16)pe;
       }
     }
-    lsum = lsum * alpha + rsum;
-    m = mn;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    lsum += rsum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T (V read transposed from LDS)
+    {
+      bf16x8 va[4 * (D / 32)];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
+      for (int kc = 0; kc < 4; ++kc) {
+        const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* p1 = sV + kr * LDSTR + db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-        bf16x8 a = cat4(lds_read_tr4(p1), lds_read_tr4(p1 + 8 * LDSTR));
-        acc[db] = mfma32(a, pb[kc], acc[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+          va[kc * (D / 32) + db] = cat4(lds_read_tr4(cV + swz<D>(kr, col)), lds_read_tr4(cV + swz<D>(kr + 8, col)));
+        }
       }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(va[kc * (D / 32) + db], pb[kc], acc[db]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * (D / 32), 0);
     }
+    buf ^= 1;
   }
 
   // epilogue: O = acc / l, lse = ln-sum-exp (natural log)

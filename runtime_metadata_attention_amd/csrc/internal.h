@@ -80,7 +80,10 @@ struct DescView {                // device pointers into a descriptor
 };
 hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, const void* v, const DescView& dv,
                            void* o, float* lse, hipStream_t stream);
-hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, float* D, hipStream_t stream);
+// D[row] and lse2[row] (lse * log2(e), +inf for empty rows) into workspace
+// D[0 .. B*H*N) and D[B*H*N .. 2*B*H*N)
+hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, const float* lse, float* D,
+                          hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
                            const void* dO, const float* D, const DescView& dv, void* dk, void* dvv,
                            hipStream_t stream);
