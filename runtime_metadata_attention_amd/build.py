@@ -30,13 +30,19 @@ COMMON = ["-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(RO
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-result"]
 
 
+# Per-file options.  The backward kernels consume most MFMA results with VALU
+# code; asking for VGPR-form MFMAs there avoids AGPR<->VGPR copies of every
+# score tile.
+FILE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) + glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str, opt: list, extra: list) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *opt, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *opt, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -107,7 +107,8 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lk = lane & 31;
   const int kt = int(blockIdx.x);  // first key tiles are seen by the most rows
   const int head = blockIdx.y, b = blockIdx.z;
@@ -198,32 +199,16 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // S = Q K^T and dP = dO V^T: two 32-row blocks, lane = key column
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    {
-      bf16x8 qa[D / 8], oa[D / 8];
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) qa[2 * c + qb] = lds_read_b128(cQ + swz<D>(qb * 32 + lk, 16 * c + 8 * h));
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oa[2 * c + qb] = lds_read_b128(cO + swz<D>(qb * 32 + lk, 16 * c + 8 * h));
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[qb] = mfma32(qa[2 * c + qb], kreg[c], s[qb]);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma32(oa[2 * c + qb], vreg[c], dp[qb]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 8, 0);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 8, 0);
-    }
+    mfma_stream<D / 4, 4, 1>(
+        [&](int i) {
+          const int j = i % (D / 8);
+          return lds_read_b128((i < D / 8 ? cQ : cO) + swz<D>((j & 1) * 32 + lk, 16 * (j >> 1) + 8 * h));
+        },
+        [&](int i, const bf16x8& a) {
+          const int j = i % (D / 8);
+          if (i < D / 8) s[j & 1] = mfma32(a, kreg[j >> 1], s[j & 1]);
+          else dp[j & 1] = mfma32(a, vreg[j >> 1], dp[j & 1]);
+        });
     if ((cs == 2) || ((ct + 1) * BQ > N))
       mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid);
     bf16x8 pb[4], db8[4];
@@ -249,42 +234,21 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
     // dV^T += dO^T P ; dK^T += Q^T dS   (k = query, in the score-register order)
-    {
-      bf16x8 ot[4 * (D / 32)], qt[4 * (D / 32)];
-#pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
-#pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk) {
+    mfma_stream<8 * (D / 32), 4, 2>(
+        [&](int i) {
+          const int j = i % (4 * (D / 32));
+          const int qc = j / (D / 32), dbk = j % (D / 32);
+          const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
           const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          ot[qc * (D / 32) + dbk] = cat4(lds_read_tr4(cO + swz<D>(kr, col)), lds_read_tr4(cO + swz<D>(kr + 8, col)));
-        }
-      }
-#pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
-#pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk) {
-          const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          qt[qc * (D / 32) + dbk] = cat4(lds_read_tr4(cQ + swz<D>(kr, col)), lds_read_tr4(cQ + swz<D>(kr + 8, col)));
-        }
-      }
-#pragma unroll
-      for (int qc = 0; qc < 4; ++qc)
-#pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk) adv[dbk] = mfma32(ot[qc * (D / 32) + dbk], pb[qc], adv[dbk]);
-#pragma unroll
-      for (int qc = 0; qc < 4; ++qc)
-#pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk) adk[dbk] = mfma32(qt[qc * (D / 32) + dbk], db8[qc], adk[dbk]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (D / 32), 0);
-#pragma unroll
-      for (int i = 0; i < 4 * (D / 32); ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * (D / 32), 0);
-    }
+          const uint16_t* t = i < 4 * (D / 32) ? cO : cQ;
+          return cat4(lds_read_tr4(t + swz<D>(kr, col)), lds_read_tr4(t + swz<D>(kr + 8, col)));
+        },
+        [&](int i, const bf16x8& a) {
+          const int j = i % (4 * (D / 32));
+          const int qc = j / (D / 32), dbk = j % (D / 32);
+          if (i < 4 * (D / 32)) adv[dbk] = mfma32(a, pb[qc], adv[dbk]);
+          else adk[dbk] = mfma32(a, db8[qc], adk[dbk]);
+        });
     buf ^= 1;
   }
 
@@ -316,7 +280,8 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lq = lane & 31;
   const int qt = p.Tq_f - 1 - int(blockIdx.x);
   const int head = blockIdx.y, b = blockIdx.z;
@@ -405,32 +370,16 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
 
     // S^T = K Q^T and dP^T = V dO^T (lane = query)
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    {
-      bf16x8 ka[D / 8], va[D / 8];
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[2 * c + kb] = lds_read_b128(cK + swz<D>(kb * 32 + lq, 16 * c + 8 * h));
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) va[2 * c + kb] = lds_read_b128(cV + swz<D>(kb * 32 + lq, 16 * c + 8 * h));
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[2 * c + kb], qreg[c], s[kb]);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(va[2 * c + kb], oreg[c], dp[kb]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 8, 0);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 8, 0);
-    }
+    mfma_stream<D / 4, 4, 1>(
+        [&](int i) {
+          const int j = i % (D / 8);
+          return lds_read_b128((i < D / 8 ? cK : cV) + swz<D>((j & 1) * 32 + lq, 16 * (j >> 1) + 8 * h));
+        },
+        [&](int i, const bf16x8& a) {
+          const int j = i % (D / 8);
+          if (i < D / 8) s[j & 1] = mfma32(a, qreg[j >> 1], s[j & 1]);
+          else dp[j & 1] = mfma32(a, oreg[j >> 1], dp[j & 1]);
+        });
     if ((cs == 2) || ((ct + 1) * BN > N))
       mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
     bf16x8 db8[4];
@@ -444,24 +393,14 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
       }
     }
     // dQ^T += K^T dS^T (K read transposed from LDS)
-    {
-      bf16x8 kt[4 * (D / 32)];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+    mfma_stream<4 * (D / 32), 4, 2>(
+        [&](int i) {
+          const int kc = i / (D / 32), db = i % (D / 32);
+          const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
           const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          kt[kc * (D / 32) + db] = cat4(lds_read_tr4(cK + swz<D>(kr, col)), lds_read_tr4(cK + swz<D>(kr + 8, col)));
-        }
-      }
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(kt[kc * (D / 32) + db], db8[kc], acc[db]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (D / 32), 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * (D / 32), 0);
-    }
+          return cat4(lds_read_tr4(cK + swz<D>(kr, col)), lds_read_tr4(cK + swz<D>(kr + 8, col)));
+        },
+        [&](int i, const bf16x8& a) { acc[i % (D / 32)] = mfma32(a, db8[i / (D / 32)], acc[i % (D / 32)]); });
     buf ^= 1;
   }
 

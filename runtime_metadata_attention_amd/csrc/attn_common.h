@@ -134,6 +134,30 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
+// A run of NM MFMAs whose A operands come from LDS: read(i) returns operand i
+// and mma(i, a) issues MFMA i.  Operand reads run G MFMAs ahead of their use
+// (a register pipeline of G + 1 operands), and the scheduling groups keep that
+// order: G reads, then (MFMA, next read) pairs.  RPO = LDS instructions per
+// operand (1 for ds_read_b128, 2 for a pair of transposed reads).
+template <int NM, int G, int RPO, class Read, class Mma>
+__device__ __forceinline__ void mfma_stream(Read&& read, Mma&& mma) {
+  constexpr int G0 = G < NM ? G : NM;
+  bf16x8 op[NM];
+#pragma unroll
+  for (int i = 0; i < G0; ++i) op[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + G < NM) op[i + G] = read(i + G);
+    mma(i, op[i]);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO * G0, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + G < NM) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO, 0);
+  }
+}
+
 // Offset, inside a 64-wide tile, of element v of 32-block blk of a score
 // tile in C layout, for the lane half h = 0 (add 4h for the other half).
 __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {

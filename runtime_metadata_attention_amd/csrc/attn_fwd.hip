@@ -52,7 +52,8 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lq = lane & 31;
   const int qt = p.Tq - 1 - int(blockIdx.x);  // the longest rows of lower-triangular masks first
   const int head = blockIdx.y, b = blockIdx.z;
@@ -136,21 +137,11 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     const uint16_t* cK = sK[buf];
     const uint16_t* cV = sV[buf];
 
-    // S^T = K Q^T for two 32-key blocks: all operand reads first, then the MFMAs
+    // S^T = K Q^T for two 32-key blocks (operand reads pipelined ahead)
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    {
-      bf16x8 ka[D / 8];
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[2 * c + kb] = lds_read_b128(cK + swz<D>(kb * 32 + lq, 16 * c + 8 * h));
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[2 * c + kb], qreg[c], s[kb]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 8, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 8, 0);
-    }
+    mfma_stream<D / 8, 4, 1>(
+        [&](int i) { return lds_read_b128(cK + swz<D>((i & 1) * 32 + lq, 16 * (i >> 1) + 8 * h)); },
+        [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
     // partial tiles (and a ragged last tile): unsigned endpoint checks
     if ((cs == 2) || ((ct + 1) * BN > N))
       mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
@@ -190,24 +181,14 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     lsum += rsum;
 
     // O^T += V^T P^T (V read transposed from LDS)
-    {
-      bf16x8 va[4 * (D / 32)];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+    mfma_stream<4 * (D / 32), 4, 2>(
+        [&](int i) {
+          const int kc = i / (D / 32), db = i % (D / 32);
+          const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
           const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          va[kc * (D / 32) + db] = cat4(lds_read_tr4(cV + swz<D>(kr, col)), lds_read_tr4(cV + swz<D>(kr + 8, col)));
-        }
-      }
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(va[kc * (D / 32) + db], pb[kc], acc[db]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (D / 32), 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * (D / 32), 0);
-    }
+          return cat4(lds_read_tr4(cV + swz<D>(kr, col)), lds_read_tr4(cV + swz<D>(kr + 8, col)));
+        },
+        [&](int i, const bf16x8& a) { acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]); });
     buf ^= 1;
   }
 

@@ -8,7 +8,7 @@
 
 #include <hip/hip_runtime_api.h>
 
-#include "../../include/compilemask.h"
+#include "compilemask.h"
 #include "program.h"
 
 struct cm_spec {
