@@ -101,11 +101,14 @@ template <int D, int BK, bool CAUSAL>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = BK / 32;
   static_assert(NW >= 2, "two waves copy lse2 and D");
-  // Q and dO tiles (double-buffered, swizzled) and the tile's lse2 / D rows
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sO[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+  // Q and dO tiles (three stages, swizzled) and the tile's lse2 / D rows.
+  // Stage t % 3 holds tile t: tile t's scores are computed while tile t - 1's
+  // dV/dK contributions (which read stage (t-1) % 3) overlap the softmax
+  // math, and tile t + 1 is copied into the third stage.
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[3][BQ * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sO[3][BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL[3][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[3][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
@@ -188,12 +191,32 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   bool have = next_tile(tile, state);
   if (have) issue(tile, 0);
   const int g = lane >> 4, gi = lane & 15;
+  // dV^T += dO^T P ; dK^T += Q^T dS of one tile (k = query, in the
+  // score-register order), as an MFMA stream with VPM VALU slots per MFMA
+  auto dvdk_reads = [&](int pbuf) {
+    return [&, pbuf](int i) {
+      const int j = i % (4 * (D / 32));
+      const int qc = j / (D / 32), dbk = j % (D / 32);
+      const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
+      const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
+      const uint16_t* t = i < 4 * (D / 32) ? sO[pbuf] : sQ[pbuf];
+      return cat4(lds_read_tr4(t + swz<D>(kr, col)), lds_read_tr4(t + swz<D>(kr + 8, col)));
+    };
+  };
+  bf16x8 ppb[4], pdb[4];  // previous tile's P and dS (bf16); zero before the first tile
+#pragma unroll
+  for (int qc = 0; qc < 4; ++qc) {
+    ppb[qc] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    pdb[qc] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+  int pbuf = 0;
+  const bool any_tile = have;
   while (have) {
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
     wait_vmem();
     __syncthreads();
-    if (have) issue(tile, buf ^ 1);
+    if (have) issue(tile, buf == 2 ? 0 : buf + 1);
     const uint16_t* cQ = sQ[buf];
     const uint16_t* cO = sO[buf];
 
@@ -211,15 +234,40 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
         });
     if ((cs == 2) || ((ct + 1) * BQ > N))
       mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid);
+
+    // P and dS of this tile (VALU), overlapped with the previous tile's
+    // dV/dK MFMAs: eight fenced chunks, each with four MFMAs (operands read
+    // four MFMAs ahead) and the softmax-gradient math of four score elements
+    // (their lse and D rows read one chunk ahead).
     bf16x8 pb[4], db8[4];
-    const float* cL = sL[buf];
-    const float* cD = sD[buf];
+    {
+      const float* cL = sL[buf];
+      const float* cD = sD[buf];
+      constexpr int NM = 8 * (D / 32), G = 4, MPC = NM / 8;
+      auto rd = dvdk_reads(pbuf);
+      bf16x8 op[NM];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      for (int i = 0; i < G; ++i) op[i] = rd(i);
+      float4 l4n = *reinterpret_cast<const float4*>(cL + 4 * h);
+      float4 d4n = *reinterpret_cast<const float4*>(cD + 4 * h);
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const float4 l4 = *reinterpret_cast<const float4*>(cL + qb * 32 + vg * 8 + 4 * h);
-        const float4 d4 = *reinterpret_cast<const float4*>(cD + qb * 32 + vg * 8 + 4 * h);
+      for (int c = 0; c < 8; ++c) {
+        const int qb = c >> 2, vg = c & 3;
+        const float4 l4 = l4n, d4 = d4n;
+        if (c < 7) {
+          const int nqb = (c + 1) >> 2, nvg = (c + 1) & 3;
+          l4n = *reinterpret_cast<const float4*>(cL + nqb * 32 + nvg * 8 + 4 * h);
+          d4n = *reinterpret_cast<const float4*>(cD + nqb * 32 + nvg * 8 + 4 * h);
+        }
+#pragma unroll
+        for (int m = 0; m < MPC; ++m) {
+          const int i = c * MPC + m;
+          if (i + G < NM) op[i + G] = rd(i + G);
+          const int j = i % (4 * (D / 32));
+          const int qc = j / (D / 32), dbk = j % (D / 32);
+          if (i < 4 * (D / 32)) adv[dbk] = mfma32(op[i], ppb[qc], adv[dbk]);
+          else adk[dbk] = mfma32(op[i], pdb[qc], adk[dbk]);
+        }
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -231,25 +279,22 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
           pb[qc][ee] = (__bf16)pe;
           db8[qc][ee] = (__bf16)ds;
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // dV^T += dO^T P ; dK^T += Q^T dS   (k = query, in the score-register order)
-    mfma_stream<8 * (D / 32), 4, 2>(
-        [&](int i) {
-          const int j = i % (4 * (D / 32));
-          const int qc = j / (D / 32), dbk = j % (D / 32);
-          const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
-          const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          const uint16_t* t = i < 4 * (D / 32) ? cO : cQ;
-          return cat4(lds_read_tr4(t + swz<D>(kr, col)), lds_read_tr4(t + swz<D>(kr + 8, col)));
-        },
-        [&](int i, const bf16x8& a) {
-          const int j = i % (4 * (D / 32));
-          const int qc = j / (D / 32), dbk = j % (D / 32);
-          if (i < 4 * (D / 32)) adv[dbk] = mfma32(a, pb[qc], adv[dbk]);
-          else adk[dbk] = mfma32(a, db8[qc], adk[dbk]);
-        });
-    buf ^= 1;
+#pragma unroll
+    for (int qc = 0; qc < 4; ++qc) { ppb[qc] = pb[qc]; pdb[qc] = db8[qc]; }
+    pbuf = buf;
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+  // the last tile's dV/dK (its stage is still intact: no copy was issued after it)
+  if (any_tile) {
+    mfma_stream<8 * (D / 32), 4, 2>(dvdk_reads(pbuf), [&](int i, const bf16x8& a) {
+      const int j = i % (4 * (D / 32));
+      const int qc = j / (D / 32), dbk = j % (D / 32);
+      if (i < 4 * (D / 32)) adv[dbk] = mfma32(a, ppb[qc], adv[dbk]);
+      else adk[dbk] = mfma32(a, pdb[qc], adk[dbk]);
+    });
   }
 
   if (kvalid) {

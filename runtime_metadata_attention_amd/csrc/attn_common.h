@@ -158,6 +158,32 @@ __device__ __forceinline__ void mfma_stream(Read&& read, Mma&& mma) {
   }
 }
 
+constexpr int kSchedValu = 0x002;
+
+// mfma_stream whose MFMAs are also interleaved with VPM VALU instructions
+// each: independent VALU work written before the call (in program order) is
+// spread over the MFMA stream, so vector math and matrix cores overlap inside
+// one wave.
+template <int NM, int G, int RPO, int VPM, class Read, class Mma>
+__device__ __forceinline__ void mfma_stream_valu(Read&& read, Mma&& mma) {
+  constexpr int G0 = G < NM ? G : NM;
+  bf16x8 op[NM];
+#pragma unroll
+  for (int i = 0; i < G0; ++i) op[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + G < NM) op[i + G] = read(i + G);
+    mma(i, op[i]);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO * G0, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + G < NM) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
+  }
+}
+
 // Offset, inside a 64-wide tile, of element v of 32-block blk of a score
 // tile in C layout, for the lane half h = 0 (add 4h for the other half).
 __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
