@@ -113,8 +113,9 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lk = lane & 31;
-  const int kt = int(blockIdx.x);  // first key tiles are seen by the most rows
-  const int head = blockIdx.y, b = blockIdx.z;
+  int kt, bh;
+  xcd_coords(int(blockIdx.x), p.Tk_b, p.B * p.H, kt, bh);  // first key tiles are seen by the most rows
+  const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;
   const int k0 = kt * BK;
   const int key = k0 + wave * 32 + lk;
@@ -328,8 +329,10 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lq = lane & 31;
-  const int qt = p.Tq_f - 1 - int(blockIdx.x);
-  const int head = blockIdx.y, b = blockIdx.z;
+  int kx, bh;
+  xcd_coords(int(blockIdx.x), p.Tq_f, p.B * p.H, kx, bh);
+  const int qt = p.Tq_f - 1 - kx;
+  const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;
   const int q0 = qt * BM;
   const int q = q0 + wave * 32 + lq;
@@ -516,7 +519,7 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
   p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dvv);
-  dim3 grid(p.Tk_b, a.H, a.B);
+  dim3 grid(p.Tk_b * a.H * a.B);
   const bool c = a.causal != 0;
 #define CM_DKDV(DD, BKK)                                                                              \
   do {                                                                                               \
@@ -540,7 +543,7 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
   p.D = D;
   p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dq = static_cast<uint16_t*>(dq);
-  dim3 grid(p.Tq_f, a.H, a.B);
+  dim3 grid(p.Tq_f * a.H * a.B);
   const bool c = a.causal != 0;
 #define CM_DQ(DD, BMM)                                                                             \
   do {                                                                                            \

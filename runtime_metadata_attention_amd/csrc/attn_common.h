@@ -240,6 +240,25 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr,
   }
 }
 
+// XCD-aware work-group order.  MI355X deals consecutive work-group ids
+// round-robin to its 8 XCDs, each with its own L2.  With a 1-D grid of
+// tiles * hb work-groups (hb = samples x heads), ids are remapped so that
+// every (sample, head) is handled by one XCD (when hb is a multiple of 8):
+// the tiles of one head that run at the same time then stream the same
+// K/V (or Q/dO) tiles through the same L2.  Within a head, tiles are visited
+// in the order `tile_of(k)`, k = 0, 1, ...
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_coords(int w, int tiles, int hb, int& k, int& bh) {
+  if (hb % kXcds == 0) {
+    const int xcd = w % kXcds, local = w / kXcds;
+    bh = xcd + kXcds * (local / tiles);
+    k = local % tiles;
+  } else {
+    bh = w / tiles;
+    k = w % tiles;
+  }
+}
+
 // Visit the non-empty tiles of one bitmap row (codes 1 full, 2 partial).
 struct TileIter {
   const uint32_t* words;

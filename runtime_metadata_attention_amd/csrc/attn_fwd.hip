@@ -55,8 +55,10 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lq = lane & 31;
-  const int qt = p.Tq - 1 - int(blockIdx.x);  // the longest rows of lower-triangular masks first
-  const int head = blockIdx.y, b = blockIdx.z;
+  int kx, bh;
+  xcd_coords(int(blockIdx.x), p.Tq, p.B * p.H, kx, bh);
+  const int qt = p.Tq - 1 - kx;  // the longest rows of lower-triangular masks first
+  const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;
   const int q0 = qt * BM;
   const int q = q0 + wave * 32 + lq;
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
 
 template <int D, int BM, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  dim3 grid(p.Tq, p.H, p.B);
+  dim3 grid(p.Tq * p.H * p.B);
   hipLaunchKernelGGL((attn_fwd_kernel<D, BM, CAUSAL>), grid, dim3(BM * 2), 0, stream, p);
   return hipGetLastError();
 }
