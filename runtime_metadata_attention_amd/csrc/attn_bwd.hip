@@ -323,8 +323,11 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 template <int D, int BM, bool CAUSAL>
 __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BM / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BN * D];
+  // K and V tiles in three stages: tile t's scores are computed while tile
+  // t - 1's dQ MFMAs (reading K of stage (t-1) % 3) overlap the dS math, and
+  // tile t + 1 is copied into the third stage.
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[3][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[3][BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
@@ -404,14 +407,29 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
     dma.issue(rV, sV[0], uint32_t(tile) * tile_bytes);
   }
   const int g = lane >> 4, gi = lane & 15;
+  // dQ^T += K^T dS^T of one tile (K read transposed from LDS)
+  auto dq_reads = [&](int kbuf) {
+    return [&, kbuf](int i) {
+      const int kc = i / (D / 32), db = i % (D / 32);
+      const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
+      const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+      return cat4(lds_read_tr4(sK[kbuf] + swz<D>(kr, col)), lds_read_tr4(sK[kbuf] + swz<D>(kr + 8, col)));
+    };
+  };
+  bf16x8 pdb[4];  // previous tile's dS (bf16); zero before the first tile
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) pdb[kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  int pbuf = 0;
+  const bool any_tile = have;
   while (have) {
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
     wait_vmem();
     __syncthreads();
     if (have) {
-      dma.issue(rK, sK[buf ^ 1], uint32_t(tile) * tile_bytes);
-      dma.issue(rV, sV[buf ^ 1], uint32_t(tile) * tile_bytes);
+      const int nb = buf == 2 ? 0 : buf + 1;
+      dma.issue(rK, sK[nb], uint32_t(tile) * tile_bytes);
+      dma.issue(rV, sV[nb], uint32_t(tile) * tile_bytes);
     }
     const uint16_t* cK = sK[buf];
     const uint16_t* cV = sV[buf];
@@ -430,26 +448,45 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
         });
     if ((cs == 2) || ((ct + 1) * BN > N))
       mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
+
+    // dS of this tile (VALU) in eight fenced chunks of four elements, each
+    // overlapped with MPC of the previous tile's dQ MFMAs
     bf16x8 db8[4];
+    {
+      constexpr int NM = 4 * (D / 32), G = 4, MPC = NM / 8;
+      auto rd = dq_reads(pbuf);
+      bf16x8 op[NM];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < G; ++i) op[i] = rd(i);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
-        const float ds = pe * (dp[kb][v] - Dq);
-        db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int m = 0; m < MPC; ++m) {
+          const int i = c * MPC + m;
+          if (i + G < NM) op[i + G] = rd(i + G);
+          acc[i % (D / 32)] = mfma32(op[i], pdb[i / (D / 32)], acc[i % (D / 32)]);
+        }
+        const int kb = c >> 2, vg = c & 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = vg * 4 + e;
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
+          const float ds = pe * (dp[kb][v] - Dq);
+          db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // dQ^T += K^T dS^T (K read transposed from LDS)
-    mfma_stream<4 * (D / 32), 4, 2>(
-        [&](int i) {
-          const int kc = i / (D / 32), db = i % (D / 32);
-          const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
-          const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          return cat4(lds_read_tr4(cK + swz<D>(kr, col)), lds_read_tr4(cK + swz<D>(kr + 8, col)));
-        },
-        [&](int i, const bf16x8& a) { acc[i % (D / 32)] = mfma32(a, db8[i / (D / 32)], acc[i % (D / 32)]); });
-    buf ^= 1;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) pdb[kc] = db8[kc];
+    pbuf = buf;
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+  // the last tile's dQ (its stage is still intact: no copy was issued after it)
+  if (any_tile) {
+    mfma_stream<4 * (D / 32), 4, 2>(dq_reads(pbuf), [&](int i, const bf16x8& a) {
+      acc[i % (D / 32)] = mfma32(a, pdb[i / (D / 32)], acc[i % (D / 32)]);
+    });
   }
 
   if (qvalid) {
