@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--workload", default="reward_model_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--causal-path", action="store_true", help="time the maskless causal path (causal masks only)")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload (and the causal comparator) and write one JSON line per run "
+                         "to stderr; the stdout line stays the default workload's")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this path has no multi-GPU mode (asked for {a.gpus}).",
@@ -122,7 +125,23 @@ def main():
     from runtime_metadata_attention_amd import specs
     from workloads import WORKLOADS, make_metadata, make_tensors
 
-    w = WORKLOADS[a.workload]
+    if a.all:
+        for name in WORKLOADS:
+            for causal in ([False, True] if WORKLOADS[name].mask == "causal" else [False]):
+                line = measure(name, causal, a.steps, a.warmup, cpu=False)
+                print("[bench-all] " + json.dumps(line), file=sys.stderr, flush=True)
+    line = measure(a.workload, a.causal_path, a.steps, a.warmup, cpu=not a.no_cpu_baseline)
+    print(json.dumps(line), flush=True)
+
+
+def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool) -> dict:
+    import torch
+
+    import runtime_metadata_attention_amd as cm
+    from runtime_metadata_attention_amd import specs
+    from workloads import WORKLOADS, make_metadata, make_tensors
+
+    w = WORKLOADS[workload]
     md = make_metadata(w)
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} tiles={w.tiles}")
     t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
@@ -132,12 +151,12 @@ def main():
     spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
     desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev)
     dmd = cm.device_metadata(md, dev)
-    args = cm.attn_args(q, causal=a.causal_path)
+    args = cm.attn_args(q, causal=causal_path)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device=dev)
-    use_desc = None if a.causal_path else desc
+    use_desc = None if causal_path else desc
 
     names = ["preprocess_kernel", "attn_fwd_kernel", "bwd_dot_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
 
@@ -146,7 +165,8 @@ def main():
             if events is not None:
                 events[i].record()
         mark(0)
-        cm.cm_build_descriptor(spec, dmd, desc)
+        if not causal_path:  # the maskless causal comparator needs no descriptor
+            cm.cm_build_descriptor(spec, dmd, desc)
         mark(1)
         cm.cm_attn_fwd(args, q, k, v, use_desc, o, lse)
         mark(2)
@@ -154,24 +174,25 @@ def main():
             cm.cm_attn_bwd_stage(s, args, q, k, v, o, lse, do, use_desc, dq, dk, dv, ws)
             mark(3 + s)
 
-    for i in range(a.warmup):
+    cm.cm_build_descriptor(spec, dmd, desc)  # (also counts V for the causal comparator)
+    for i in range(warmup):
         step()
     torch.cuda.synchronize()
     V = visible_pairs(desc, w.H)
     log(f"warmup done; visible pairs V = {V}")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.zeros((a.steps, 5))
+    per = np.zeros((steps, 5))
     for i, e in enumerate(evs):
         for j in range(5):
             per[i, j] = e[j].elapsed_time(e[j + 1])  # ms
     avg = per.mean(axis=0)
-    ms_step = wall * 1e3 / a.steps
+    ms_step = wall * 1e3 / steps
     log("per-kernel ms: " + ", ".join(f"{n}={x:.4f}" for n, x in zip(names, avg)))
 
     d = w.d
@@ -191,8 +212,8 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -200,7 +221,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded metadata and N(0,1) bf16 tensors)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tiles": list(w.tiles),
-                   "seed": w.seed, "visible_pairs": V, "path": "causal" if a.causal_path else "descriptor"},
+                   "seed": w.seed, "visible_pairs": V, "path": "causal" if causal_path else "descriptor"},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "preprocess_us": round(times["preprocess_kernel"] * 1e3, 2),
         "preprocess_GBps": round(pre_bytes / (times["preprocess_kernel"] * 1e-3) / 1e9, 1),
@@ -211,12 +232,12 @@ def main():
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
-    if not a.no_cpu_baseline:
+    if cpu:
         log("timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(w.name)
         line["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()
                                 if k != "seconds"}
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":
