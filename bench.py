@@ -10,6 +10,17 @@ visible (query, key) pairs of the batch summed over heads (4 d V forward,
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Prints one JSON line on stdout.  Progress goes to stderr.
+
+HBM traffic of the dominant kernel comes from rocprofv3 counter runs:
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/fetch -o run -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/write -o run -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_fetch -o run -- python bench.py --copy-calibration
+    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_write -o run -- python bench.py --copy-calibration
+    python bench.py --record-traffic OUT
+
+The copy runs time a plain device-to-device copy of known size; the ratio of
+its true bytes to what the counters report scales the kernel's counts.
 """
 from __future__ import annotations
 
@@ -57,6 +68,74 @@ def traffic_for(kernel: str, workload: str):
     if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES (three launches) for the counter runs."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def _pmc_per_dispatch(csv_dir: str, counter: str):
+    """{kernel name: [counter value per dispatch]} from a rocprofv3 csv directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def record_traffic(out_dir: str, workload: str = "reward_model_32k"):
+    """Scale the FETCH_SIZE / WRITE_SIZE counts (KiB per dispatch) of the attention kernels by the copy
+    calibration and write profiles/traffic.json; prints a markdown summary."""
+    cf = _pmc_per_dispatch(os.path.join(out_dir, "copy_fetch"), "FETCH_SIZE")
+    cw = _pmc_per_dispatch(os.path.join(out_dir, "copy_write"), "WRITE_SIZE")
+    copy_name = max(cf, key=lambda n: max(cf[n]))
+    kib_f, kib_w = max(cf[copy_name]), max(cw[copy_name])
+    f_fetch = COPY_BYTES / (kib_f * 1024.0)
+    f_write = COPY_BYTES / (kib_w * 1024.0)
+    kf = _pmc_per_dispatch(os.path.join(out_dir, "fetch"), "FETCH_SIZE")
+    kw = _pmc_per_dispatch(os.path.join(out_dir, "write"), "WRITE_SIZE")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    lines = [f"copy kernel `{copy_name[:60]}`: {COPY_BYTES} B read and written; FETCH_SIZE {kib_f:.0f} KiB "
+             f"(factor {f_fetch:.4f}), WRITE_SIZE {kib_w:.0f} KiB (factor {f_write:.4f})", "",
+             "| kernel | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | HBM bytes per launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for kernel in KERNEL_SOURCES:
+        names = [n for n in kf if kernel in n]
+        if not names:
+            continue
+        fv = [x for n in names for x in kf[n]]
+        wv = [x for n in names for x in kw.get(n, [])]
+        mf, mw = float(np.mean(fv)), float(np.mean(wv)) if wv else 0.0
+        total = mf * 1024.0 * f_fetch + mw * 1024.0 * f_write
+        rec[f"{kernel}@{workload}"] = {"source_hash": source_hash(kernel), "bytes_per_launch": round(total),
+                                       "fetch_kib": round(mf, 1), "write_kib": round(mw, 1),
+                                       "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5)}
+        lines.append(f"| `{kernel}` | {len(fv)} | {mf:.0f} | {mw:.0f} | {total:.4g} |")
+    json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
 
 
 def visible_pairs(desc, H: int) -> int:
@@ -113,7 +192,15 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="also time every workload (and the causal comparator) and write one JSON line per run "
                          "to stderr; the stdout line stays the default workload's")
+    ap.add_argument("--copy-calibration", action="store_true", help="only run the plain copy for counter scaling")
+    ap.add_argument("--record-traffic", metavar="DIR", help="write profiles/traffic.json from counter runs in DIR")
     a = ap.parse_args()
+    if a.record_traffic:
+        record_traffic(a.record_traffic, a.workload)
+        return
+    if a.copy_calibration:
+        copy_calibration()
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this path has no multi-GPU mode (asked for {a.gpus}).",
               file=sys.stderr)

@@ -95,18 +95,55 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ shared pieces
+
+// Per-lane byte offsets of the LDS operand reads inside one swizzled BR x D
+// tile (row-major, D bf16 per row).
+//   row[m]     : MFMA A-operand rows, ds_read_b128 of row (lane % 32), d chunk
+//                16 m + 8 h; the second 32-row block adds 32 D * 2 bytes.
+//   tr[db][hf] : transposed reads for the k-major operand of d block db: the
+//                address lane (g, gi) supplies for rows 8 hf + 4 (g / 2) +
+//                gi / 4, columns 32 db + 16 (g % 2) + 4 (gi % 4); each further
+//                16-row chunk adds 16 D * 2 bytes.
+// The swizzle only depends on the low four row bits, so the row-block and
+// 16-row offsets are immediates of the LDS instructions.
+template <int D>
+struct LdsOffsets {
+  uint32_t row[D / 16];
+  uint32_t tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, lr = lane & 31, g = lane >> 4, gi = lane & 15;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) row[m] = uint32_t(swz<D>(lr, 16 * m + 8 * h)) * 2u;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        tr[db][hf] = uint32_t(swz<D>(8 * hf + 4 * (g >> 1) + (gi >> 2), db * 32 + 16 * (g & 1) + 4 * (gi & 3))) * 2u;
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_b128_at(const char* p) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ bf16x8 lds_tr8_at(const char* p0, const char* p1) {
+  return cat4(lds_read_tr4(reinterpret_cast<const uint16_t*>(p0)), lds_read_tr4(reinterpret_cast<const uint16_t*>(p1)));
+}
+
 // ------------------------------------------------------------------ dK / dV
 
 template <int D, int BK, bool CAUSAL>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = BK / 32;
   static_assert(NW >= 2, "two waves copy lse2 and D");
-  // Q and dO tiles (three stages, swizzled) and the tile's lse2 / D rows.
-  // Stage t % 3 holds tile t: tile t's scores are computed while tile t - 1's
-  // dV/dK contributions (which read stage (t-1) % 3) overlap the softmax
-  // math, and tile t + 1 is copied into the third stage.
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[3][BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sO[3][BQ * D];
+  constexpr int TILE = BQ * D;                 // bf16 elements of one Q or dO tile
+  constexpr int TB = TILE * 2;                 // its bytes
+  // Q and dO tiles (three stages, swizzled; stage x holds Q then dO) and the
+  // tile's lse2 / D rows.  Stage t % 3 holds tile t: tile t's scores are
+  // computed while tile t - 1's dV/dK contributions (which read stage
+  // (t-1) % 3) overlap the softmax-gradient math, and tile t + 1 is copied
+  // into the third stage.
+  __shared__ __attribute__((aligned(1024))) uint16_t sQO[3][2][TILE];
   __shared__ __attribute__((aligned(16))) float sL[3][BQ];
   __shared__ __attribute__((aligned(16))) float sD[3][BQ];
 
@@ -130,11 +167,13 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   dma.init(wave, lane, p.sn);
   const uint32_t tile_bytes = uint32_t(BQ * p.sn * 2);
   auto issue = [&](int tile, int bf) {
-    dma.issue(rQ, sQ[bf], uint32_t(tile) * tile_bytes);
-    dma.issue(rO, sO[bf], uint32_t(tile) * tile_bytes);
+    dma.issue(rQ, sQO[bf][0], uint32_t(tile) * tile_bytes);
+    dma.issue(rO, sQO[bf][1], uint32_t(tile) * tile_bytes);
     if (wave == 0) dma_row_floats(rL, sL[bf], lane, uint32_t(tile * BQ * 4));
     else if (wave == 1) dma_row_floats(rDv, sD[bf], lane, uint32_t(tile * BQ * 4));
   };
+  LdsOffsets<D> lo;
+  lo.init(lane);
 
   // this wave's keys as B operands: K[key][16c + 8h ..], V[key][16c + 8h ..]
   bf16x8 kreg[D / 16], vreg[D / 16];
@@ -191,18 +230,14 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   int tile = 0, state = 0, buf = 0;
   bool have = next_tile(tile, state);
   if (have) issue(tile, 0);
-  const int g = lane >> 4, gi = lane & 15;
-  // dV^T += dO^T P ; dK^T += Q^T dS of one tile (k = query, in the
-  // score-register order), as an MFMA stream with VPM VALU slots per MFMA
-  auto dvdk_reads = [&](int pbuf) {
-    return [&, pbuf](int i) {
-      const int j = i % (4 * (D / 32));
-      const int qc = j / (D / 32), dbk = j % (D / 32);
-      const int kr = qc * 16 + 4 * (g >> 1) + (gi >> 2);
-      const int col = dbk * 32 + 16 * (g & 1) + 4 * (gi & 3);
-      const uint16_t* t = i < 4 * (D / 32) ? sO[pbuf] : sQ[pbuf];
-      return cat4(lds_read_tr4(t + swz<D>(kr, col)), lds_read_tr4(t + swz<D>(kr + 8, col)));
-    };
+  const char* lds0 = reinterpret_cast<const char*>(&sQO[0][0][0]);
+  constexpr int NC = 4 * (D / 32);  // MFMAs of one of dV, dK per tile
+  // dV^T += dO^T P (MFMAs 0..NC-1), dK^T += Q^T dS (NC..2NC-1) of the tile in
+  // stage `st`; k = query, in the score-register order
+  auto dvdk_read = [&](const char* st, int i) {
+    const int j = i % NC, qc = j / (D / 32), dbk = j % (D / 32);
+    const char* t = st + (i < NC ? TB : 0) + qc * (16 * D * 2);
+    return lds_tr8_at(t + lo.tr[dbk][0], t + lo.tr[dbk][1]);
   };
   bf16x8 ppb[4], pdb[4];  // previous tile's P and dS (bf16); zero before the first tile
 #pragma unroll
@@ -218,63 +253,94 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     wait_vmem();
     __syncthreads();
     if (have) issue(tile, buf == 2 ? 0 : buf + 1);
-    const uint16_t* cQ = sQ[buf];
-    const uint16_t* cO = sO[buf];
+    const char* cur = lds0 + buf * (2 * TB);
+    const float* cL = sL[buf];
+    const float* cD = sD[buf];
 
-    // S = Q K^T and dP = dO V^T: two 32-row blocks, lane = key column
+    // S = Q K^T (NS MFMAs), then dP = dO V^T (NS MFMAs) in eight fenced
+    // chunks, each also computing four probabilities P = exp2(S log2e/sqrt(d)
+    // - lse2) of the finished S (lane = key column; its lse2 rows are read
+    // one chunk ahead).
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    mfma_stream<D / 4, 4, 1>(
-        [&](int i) {
-          const int j = i % (D / 8);
-          return lds_read_b128((i < D / 8 ? cQ : cO) + swz<D>((j & 1) * 32 + lk, 16 * (j >> 1) + 8 * h));
-        },
-        [&](int i, const bf16x8& a) {
-          const int j = i % (D / 8);
-          if (i < D / 8) s[j & 1] = mfma32(a, kreg[j >> 1], s[j & 1]);
-          else dp[j & 1] = mfma32(a, vreg[j >> 1], dp[j & 1]);
-        });
-    if ((cs == 2) || ((ct + 1) * BQ > N))
-      mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid);
-
-    // P and dS of this tile (VALU), overlapped with the previous tile's
-    // dV/dK MFMAs: eight fenced chunks, each with four MFMAs (operands read
-    // four MFMAs ahead) and the softmax-gradient math of four score elements
-    // (their lse and D rows read one chunk ahead).
-    bf16x8 pb[4], db8[4];
     {
-      const float* cL = sL[buf];
-      const float* cD = sD[buf];
-      constexpr int NM = 8 * (D / 32), G = 4, MPC = NM / 8;
-      auto rd = dvdk_reads(pbuf);
+      constexpr int NS = D / 8, NM = 2 * NS, G = 4, MPC = NS / 8;
+      auto rd = [&](int i) {
+        const int j = i % NS;
+        return lds_b128_at(cur + (i < NS ? 0 : TB) + (j & 1) * (32 * D * 2) + lo.row[j >> 1]);
+      };
+      auto mma = [&](int i, const bf16x8& a) {
+        const int j = i % NS;
+        if (i < NS) s[j & 1] = mfma32(a, kreg[j >> 1], s[j & 1]);
+        else dp[j & 1] = mfma32(a, vreg[j >> 1], dp[j & 1]);
+      };
       bf16x8 op[NM];
 #pragma unroll
       for (int i = 0; i < G; ++i) op[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        op[i + G] = rd(i + G);
+        mma(i, op[i]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, G, 0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float4 l4n = *reinterpret_cast<const float4*>(cL + 4 * h);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int qb = c >> 2, vg = c & 3;
+        const float4 l4 = l4n;
+        if (c < 7) l4n = *reinterpret_cast<const float4*>(cL + ((c + 1) >> 2) * 32 + ((c + 1) & 3) * 8 + 4 * h);
+#pragma unroll
+        for (int m = 0; m < MPC; ++m) {
+          const int i = NS + c * MPC + m;
+          if (i + G < NM) op[i + G] = rd(i + G);
+          mma(i, op[i]);
+        }
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[qb][vg * 4 + e] = __builtin_amdgcn_exp2f(fmaf(s[qb][vg * 4 + e], p.scale_log2, -lv[e]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // partial and ragged tiles: invisible probabilities are zero
+    if ((cs == 2) || ((ct + 1) * BQ > N))
+      mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid, 0.f);
+
+    // dS = P (dP - D) of this tile and the bf16 P, dS operands, in eight
+    // fenced chunks of four elements, each overlapped with 2NC/8 of the
+    // previous tile's dV/dK MFMAs (operands read four MFMAs ahead, D one
+    // chunk ahead).
+    bf16x8 pb[4], db8[4];
+    {
+      constexpr int NM = 2 * NC, G = 4, MPC = NM / 8;
+      const char* prv = lds0 + pbuf * (2 * TB);
+      bf16x8 op[NM];
+#pragma unroll
+      for (int i = 0; i < G; ++i) op[i] = dvdk_read(prv, i);
       float4 d4n = *reinterpret_cast<const float4*>(cD + 4 * h);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int qb = c >> 2, vg = c & 3;
-        const float4 l4 = l4n, d4 = d4n;
-        if (c < 7) {
-          const int nqb = (c + 1) >> 2, nvg = (c + 1) & 3;
-          l4n = *reinterpret_cast<const float4*>(cL + nqb * 32 + nvg * 8 + 4 * h);
-          d4n = *reinterpret_cast<const float4*>(cD + nqb * 32 + nvg * 8 + 4 * h);
-        }
+        const float4 d4 = d4n;
+        if (c < 7) d4n = *reinterpret_cast<const float4*>(cD + ((c + 1) >> 2) * 32 + ((c + 1) & 3) * 8 + 4 * h);
 #pragma unroll
         for (int m = 0; m < MPC; ++m) {
           const int i = c * MPC + m;
-          if (i + G < NM) op[i + G] = rd(i + G);
-          const int j = i % (4 * (D / 32));
-          const int qc = j / (D / 32), dbk = j % (D / 32);
-          if (i < 4 * (D / 32)) adv[dbk] = mfma32(op[i], ppb[qc], adv[dbk]);
+          if (i + G < NM) op[i + G] = dvdk_read(prv, i + G);
+          const int j = i % NC, qc = j / (D / 32), dbk = j % (D / 32);
+          if (i < NC) adv[dbk] = mfma32(op[i], ppb[qc], adv[dbk]);
           else adk[dbk] = mfma32(op[i], pdb[qc], adk[dbk]);
         }
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = vg * 4 + e;
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[qb][v], p.scale_log2, -lv[e]));
+          const float pe = s[qb][v];
           const float ds = pe * (dp[qb][v] - dv4[e]);
           const int qc = qb * 2 + (v >> 3), ee = v & 7;
           pb[qc][ee] = (__bf16)pe;
@@ -290,10 +356,10 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
   // the last tile's dV/dK (its stage is still intact: no copy was issued after it)
   if (any_tile) {
-    mfma_stream<8 * (D / 32), 4, 2>(dvdk_reads(pbuf), [&](int i, const bf16x8& a) {
-      const int j = i % (4 * (D / 32));
-      const int qc = j / (D / 32), dbk = j % (D / 32);
-      if (i < 4 * (D / 32)) adv[dbk] = mfma32(a, ppb[qc], adv[dbk]);
+    const char* prv = lds0 + pbuf * (2 * TB);
+    mfma_stream<2 * NC, 4, 2>([&](int i) { return dvdk_read(prv, i); }, [&](int i, const bf16x8& a) {
+      const int j = i % NC, qc = j / (D / 32), dbk = j % (D / 32);
+      if (i < NC) adv[dbk] = mfma32(a, ppb[qc], adv[dbk]);
       else adk[dbk] = mfma32(a, pdb[qc], adk[dbk]);
     });
   }
@@ -323,11 +389,12 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 template <int D, int BM, bool CAUSAL>
 __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BM / 32;
-  // K and V tiles in three stages: tile t's scores are computed while tile
-  // t - 1's dQ MFMAs (reading K of stage (t-1) % 3) overlap the dS math, and
-  // tile t + 1 is copied into the third stage.
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[3][BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[3][BN * D];
+  constexpr int TILE = BN * D;
+  constexpr int TB = TILE * 2;
+  // K and V tiles in three stages (stage x holds K then V): tile t's scores
+  // are computed while tile t - 1's dQ MFMAs (reading K of stage (t-1) % 3)
+  // overlap the dS math, and tile t + 1 is copied into the third stage.
+  __shared__ __attribute__((aligned(1024))) uint16_t sKV[3][2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
@@ -347,6 +414,8 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   TileDma<D, BN, NW> dma;
   dma.init(wave, lane, p.sn);
   const uint32_t tile_bytes = uint32_t(BN * p.sn * 2);
+  LdsOffsets<D> lo;
+  lo.init(lane);
 
   bf16x8 qreg[D / 16], oreg[D / 16];
 #pragma unroll
@@ -403,18 +472,16 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   int tile = 0, state = 0, buf = 0;
   bool have = next_tile(tile, state);
   if (have) {
-    dma.issue(rK, sK[0], uint32_t(tile) * tile_bytes);
-    dma.issue(rV, sV[0], uint32_t(tile) * tile_bytes);
+    dma.issue(rK, sKV[0][0], uint32_t(tile) * tile_bytes);
+    dma.issue(rV, sKV[0][1], uint32_t(tile) * tile_bytes);
   }
-  const int g = lane >> 4, gi = lane & 15;
-  // dQ^T += K^T dS^T of one tile (K read transposed from LDS)
-  auto dq_reads = [&](int kbuf) {
-    return [&, kbuf](int i) {
-      const int kc = i / (D / 32), db = i % (D / 32);
-      const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
-      const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-      return cat4(lds_read_tr4(sK[kbuf] + swz<D>(kr, col)), lds_read_tr4(sK[kbuf] + swz<D>(kr + 8, col)));
-    };
+  const char* lds0 = reinterpret_cast<const char*>(&sKV[0][0][0]);
+  constexpr int NQ = 4 * (D / 32);  // dQ MFMAs per tile
+  // dQ^T += K^T dS^T of the tile in stage `st` (K read transposed)
+  auto dq_read = [&](const char* st, int i) {
+    const int kc = i / (D / 32), db = i % (D / 32);
+    const char* t = st + kc * (16 * D * 2);
+    return lds_tr8_at(t + lo.tr[db][0], t + lo.tr[db][1]);
   };
   bf16x8 pdb[4];  // previous tile's dS (bf16); zero before the first tile
 #pragma unroll
@@ -428,50 +495,82 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     if (have) {
       const int nb = buf == 2 ? 0 : buf + 1;
-      dma.issue(rK, sK[nb], uint32_t(tile) * tile_bytes);
-      dma.issue(rV, sV[nb], uint32_t(tile) * tile_bytes);
+      dma.issue(rK, sKV[nb][0], uint32_t(tile) * tile_bytes);
+      dma.issue(rV, sKV[nb][1], uint32_t(tile) * tile_bytes);
     }
-    const uint16_t* cK = sK[buf];
-    const uint16_t* cV = sV[buf];
+    const char* cur = lds0 + buf * (2 * TB);
 
-    // S^T = K Q^T and dP^T = V dO^T (lane = query)
+    // S^T = K Q^T (NS MFMAs), then dP^T = V dO^T (NS MFMAs) in eight fenced
+    // chunks, each also computing four probabilities of the finished S^T
+    // (lane = query: one lse2 per lane).
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    mfma_stream<D / 4, 4, 1>(
-        [&](int i) {
-          const int j = i % (D / 8);
-          return lds_read_b128((i < D / 8 ? cK : cV) + swz<D>((j & 1) * 32 + lq, 16 * (j >> 1) + 8 * h));
-        },
-        [&](int i, const bf16x8& a) {
-          const int j = i % (D / 8);
-          if (i < D / 8) s[j & 1] = mfma32(a, qreg[j >> 1], s[j & 1]);
-          else dp[j & 1] = mfma32(a, oreg[j >> 1], dp[j & 1]);
-        });
-    if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
-
-    // dS of this tile (VALU) in eight fenced chunks of four elements, each
-    // overlapped with MPC of the previous tile's dQ MFMAs
-    bf16x8 db8[4];
     {
-      constexpr int NM = 4 * (D / 32), G = 4, MPC = NM / 8;
-      auto rd = dq_reads(pbuf);
+      constexpr int NS = D / 8, NM = 2 * NS, G = 4, MPC = NS / 8;
+      auto rd = [&](int i) {
+        const int j = i % NS;
+        return lds_b128_at(cur + (i < NS ? 0 : TB) + (j & 1) * (32 * D * 2) + lo.row[j >> 1]);
+      };
+      auto mma = [&](int i, const bf16x8& a) {
+        const int j = i % NS;
+        if (i < NS) s[j & 1] = mfma32(a, qreg[j >> 1], s[j & 1]);
+        else dp[j & 1] = mfma32(a, oreg[j >> 1], dp[j & 1]);
+      };
       bf16x8 op[NM];
 #pragma unroll
       for (int i = 0; i < G; ++i) op[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        op[i + G] = rd(i + G);
+        mma(i, op[i]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, G, 0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int kb = c >> 2, vg = c & 3;
+#pragma unroll
+        for (int m = 0; m < MPC; ++m) {
+          const int i = NS + c * MPC + m;
+          if (i + G < NM) op[i + G] = rd(i + G);
+          mma(i, op[i]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[kb][vg * 4 + e] = __builtin_amdgcn_exp2f(fmaf(s[kb][vg * 4 + e], p.scale_log2, -lse2));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // partial and ragged tiles: invisible probabilities are zero
+    if ((cs == 2) || ((ct + 1) * BN > N))
+      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid, 0.f);
+
+    // dS^T = P^T (dP^T - D) of this tile in eight fenced chunks of four
+    // elements, each overlapped with NQ/8 of the previous tile's dQ MFMAs
+    bf16x8 db8[4];
+    {
+      constexpr int G = 4, MPC = NQ / 8;
+      const char* prv = lds0 + pbuf * (2 * TB);
+      bf16x8 op[NQ];
+#pragma unroll
+      for (int i = 0; i < G; ++i) op[i] = dq_read(prv, i);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
 #pragma unroll
         for (int m = 0; m < MPC; ++m) {
           const int i = c * MPC + m;
-          if (i + G < NM) op[i + G] = rd(i + G);
+          if (i + G < NQ) op[i + G] = dq_read(prv, i + G);
           acc[i % (D / 32)] = mfma32(op[i], pdb[i / (D / 32)], acc[i % (D / 32)]);
         }
         const int kb = c >> 2, vg = c & 3;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = vg * 4 + e;
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][v], p.scale_log2, -lse2));
-          const float ds = pe * (dp[kb][v] - Dq);
+          const float ds = s[kb][v] * (dp[kb][v] - Dq);
           db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -484,7 +583,8 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   }
   // the last tile's dQ (its stage is still intact: no copy was issued after it)
   if (any_tile) {
-    mfma_stream<4 * (D / 32), 4, 2>(dq_reads(pbuf), [&](int i, const bf16x8& a) {
+    const char* prv = lds0 + pbuf * (2 * TB);
+    mfma_stream<NQ, 4, 2>([&](int i) { return dq_read(prv, i); }, [&](int i, const bf16x8& a) {
       acc[i % (D / 32)] = mfma32(a, pdb[i / (D / 32)], acc[i % (D / 32)]);
     });
   }

@@ -158,32 +158,6 @@ __device__ __forceinline__ void mfma_stream(Read&& read, Mma&& mma) {
   }
 }
 
-constexpr int kSchedValu = 0x002;
-
-// mfma_stream whose MFMAs are also interleaved with VPM VALU instructions
-// each: independent VALU work written before the call (in program order) is
-// spread over the MFMA stream, so vector math and matrix cores overlap inside
-// one wave.
-template <int NM, int G, int RPO, int VPM, class Read, class Mma>
-__device__ __forceinline__ void mfma_stream_valu(Read&& read, Mma&& mma) {
-  constexpr int G0 = G < NM ? G : NM;
-  bf16x8 op[NM];
-#pragma unroll
-  for (int i = 0; i < G0; ++i) op[i] = read(i);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    if (i + G < NM) op[i + G] = read(i + G);
-    mma(i, op[i]);
-  }
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO * G0, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (i + G < NM) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
-  }
-}
-
 // Offset, inside a 64-wide tile, of element v of 32-block blk of a score
 // tile in C layout, for the lane half h = 0 (add 4h for the other half).
 __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
@@ -192,10 +166,12 @@ __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
 
 // Partial-tile visibility (unsigned endpoint compares) for a score tile of two
 // 32-blocks: element e is visible when (base + offset(e) - start_r) <u len_r
-// for some run r; invisible scores become -inf.  `base` is the tile's first
-// index plus 4h.  NR runs are held in registers.
+// for some run r; invisible elements become `fill` (-inf for scores before a
+// softmax, 0 for probabilities).  `base` is the tile's first index plus 4h.
+// NR runs are held in registers.
 template <int NR>
-__device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const uint32_t* rs, const uint32_t* rl) {
+__device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const uint32_t* rs, const uint32_t* rl,
+                                          float fill) {
   uint32_t off[NR > 0 ? NR : 1];
 #pragma unroll
   for (int r = 0; r < NR; ++r) off[r] = base - rs[r];
@@ -206,14 +182,15 @@ __device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const u
       bool vis = false;
 #pragma unroll
       for (int r = 0; r < NR; ++r) vis = vis | (off[r] + elem_offset(blk, v) < rl[r]);
-      s[blk][v] = vis ? s[blk][v] : -INFINITY;
+      s[blk][v] = vis ? s[blk][v] : fill;
     }
   }
 }
 
 // Same check with the runs read from memory (rows or columns with more runs
 // than the register copy holds).
-__device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, const uint2* runs, int nr, bool valid) {
+__device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, const uint2* runs, int nr, bool valid,
+                                              float fill) {
   uint32_t bits = 0;
   for (int r = 0; r < nr; ++r) {
     const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
@@ -222,21 +199,21 @@ __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, con
     for (int e = 0; e < 32; ++e) bits |= uint32_t(off + elem_offset(e >> 4, e & 15) < len) << e;
   }
 #pragma unroll
-  for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = ((bits >> e) & 1u) ? s[e >> 4][e & 15] : -INFINITY;
+  for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = ((bits >> e) & 1u) ? s[e >> 4][e & 15] : fill;
 }
 
 // Dispatch on the tile's run maximum (wave-uniform).
 template <int MAXR>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr, const uint32_t* rs,
-                                          const uint32_t* rl, const uint2* runs, bool valid) {
+                                          const uint32_t* rl, const uint2* runs, bool valid, float fill) {
   static_assert(MAXR == 4, "register copy holds 4 runs");
   switch (nr) {
-    case 0: mask_runs<0>(s, base, rs, rl); break;
-    case 1: mask_runs<1>(s, base, rs, rl); break;
-    case 2: mask_runs<2>(s, base, rs, rl); break;
-    case 3: mask_runs<3>(s, base, rs, rl); break;
-    case 4: mask_runs<4>(s, base, rs, rl); break;
-    default: mask_runs_mem(s, base, runs, nr, valid); break;
+    case 0: mask_runs<0>(s, base, rs, rl, fill); break;
+    case 1: mask_runs<1>(s, base, rs, rl, fill); break;
+    case 2: mask_runs<2>(s, base, rs, rl, fill); break;
+    case 3: mask_runs<3>(s, base, rs, rl, fill); break;
+    case 4: mask_runs<4>(s, base, rs, rl, fill); break;
+    default: mask_runs_mem(s, base, runs, nr, valid, fill); break;
   }
 }
 

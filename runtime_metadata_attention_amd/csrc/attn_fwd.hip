@@ -146,7 +146,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
     // partial tiles (and a ragged last tile): unsigned endpoint checks
     if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid);
+      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid, -INFINITY);
 
     // online softmax in the log2 domain, scale folded into the exponent.  The
     // running max is only moved (and O rescaled) when some row's max grew by
