@@ -62,7 +62,8 @@ struct BwdParams {
   const uint32_t* col_tkmax;
 };
 
-constexpr int MAXR = 4;
+constexpr int MAXR = 4;    // column runs held in registers by the dK/dV kernel
+constexpr int MAXR_Q = 2;  // row runs held in registers by the dQ kernel (more are read from memory)
 constexpr int BQ = 64;  // query rows per step of the dK/dV kernel
 constexpr int BN = 64;  // keys per step of the dQ kernel
 
@@ -101,25 +102,35 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
 // tile (row-major, D bf16 per row).
 //   row[m]     : MFMA A-operand rows, ds_read_b128 of row (lane % 32), d chunk
 //                16 m + 8 h; the second 32-row block adds 32 D * 2 bytes.
-//   tr[db][hf] : transposed reads for the k-major operand of d block db: the
+//   tr(db, hf) : transposed reads for the k-major operand of d block db: the
 //                address lane (g, gi) supplies for rows 8 hf + 4 (g / 2) +
 //                gi / 4, columns 32 db + 16 (g % 2) + 4 (gi % 4); each further
 //                16-row chunk adds 16 D * 2 bytes.
 // The swizzle only depends on the low four row bits, so the row-block and
 // 16-row offsets are immediates of the LDS instructions.
-template <int D>
+// With COMPACT, the second half (hf = 1, eight rows further) is formed on the
+// fly: it differs from the first by a per-lane constant, since the swizzle of
+// rows 8..15 flips chunk bit 1, which for these lanes is g % 2 whatever db
+// is.  That saves D / 32 registers for one add per transposed pair.
+template <int D, bool COMPACT>
 struct LdsOffsets {
   uint32_t row[D / 16];
-  uint32_t tr[D / 32][2];
+  uint32_t tr0[D / 32];
+  uint32_t tr1[COMPACT ? 1 : D / 32];
   __device__ __forceinline__ void init(int lane) {
     const int h = lane >> 5, lr = lane & 31, g = lane >> 4, gi = lane & 15;
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) row[m] = uint32_t(swz<D>(lr, 16 * m + 8 * h)) * 2u;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        tr[db][hf] = uint32_t(swz<D>(8 * hf + 4 * (g >> 1) + (gi >> 2), db * 32 + 16 * (g & 1) + 4 * (gi & 3))) * 2u;
+    for (int db = 0; db < D / 32; ++db) {
+      tr0[db] = uint32_t(swz<D>(4 * (g >> 1) + (gi >> 2), db * 32 + 16 * (g & 1) + 4 * (gi & 3))) * 2u;
+      if (!COMPACT) tr1[db] = uint32_t(swz<D>(8 + 4 * (g >> 1) + (gi >> 2), db * 32 + 16 * (g & 1) + 4 * (gi & 3))) * 2u;
+    }
+    if (COMPACT) tr1[0] = uint32_t(swz<D>(8 + 4 * (g >> 1) + (gi >> 2), 16 * (g & 1) + 4 * (gi & 3))) * 2u - tr0[0];
+  }
+  __device__ __forceinline__ uint32_t tr(int db, int hf) const {
+    if (!hf) return tr0[db];
+    return COMPACT ? tr0[db] + tr1[0] : tr1[COMPACT ? 0 : db];
   }
 };
 
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     if (wave == 0) dma_row_floats(rL, sL[bf], lane, uint32_t(tile * BQ * 4));
     else if (wave == 1) dma_row_floats(rDv, sD[bf], lane, uint32_t(tile * BQ * 4));
   };
-  LdsOffsets<D> lo;
+  LdsOffsets<D, false> lo;
   lo.init(lane);
 
   // this wave's keys as B operands: K[key][16c + 8h ..], V[key][16c + 8h ..]
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto dvdk_read = [&](const char* st, int i) {
     const int j = i % NC, qc = j / (D / 32), dbk = j % (D / 32);
     const char* t = st + (i < NC ? TB : 0) + qc * (16 * D * 2);
-    return lds_tr8_at(t + lo.tr[dbk][0], t + lo.tr[dbk][1]);
+    return lds_tr8_at(t + lo.tr(dbk, 0), t + lo.tr(dbk, 1));
   };
   bf16x8 ppb[4], pdb[4];  // previous tile's P and dS (bf16); zero before the first tile
 #pragma unroll
@@ -387,14 +398,14 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 // ------------------------------------------------------------------ dQ
 
 template <int D, int BM, bool CAUSAL>
-__global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BM / 32;
   constexpr int TILE = BN * D;
   constexpr int TB = TILE * 2;
-  // K and V tiles in three stages (stage x holds K then V): tile t's scores
-  // are computed while tile t - 1's dQ MFMAs (reading K of stage (t-1) % 3)
-  // overlap the dS math, and tile t + 1 is copied into the third stage.
-  __shared__ __attribute__((aligned(1024))) uint16_t sKV[3][2][TILE];
+  // K and V tiles in two stages (stage x holds K then V): tile t + 1 is
+  // copied into the other stage while tile t is processed.  Two work-groups
+  // share a CU, so one's vector math overlaps the other's matrix work.
+  __shared__ __attribute__((aligned(1024))) uint16_t sKV[2][2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   TileDma<D, BN, NW> dma;
   dma.init(wave, lane, p.sn);
   const uint32_t tile_bytes = uint32_t(BN * p.sn * 2);
-  LdsOffsets<D> lo;
+  LdsOffsets<D, true> lo;
   lo.init(lane);
 
   bf16x8 qreg[D / 16], oreg[D / 16];
@@ -432,18 +443,18 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   const float Dq = qvalid ? p.D[rbase + q] : 0.f;
 
   int nr;
-  uint32_t rs[MAXR], rl[MAXR];
+  uint32_t rs[MAXR_Q], rl[MAXR_Q];
   const uint2* myruns = nullptr;
   if (CAUSAL) {
     nr = 1;
     rs[0] = 0; rl[0] = uint32_t(q + 1);
 #pragma unroll
-    for (int r = 1; r < MAXR; ++r) { rs[r] = 0; rl[r] = 0; }
+    for (int r = 1; r < MAXR_Q; ++r) { rs[r] = 0; rl[r] = 0; }
   } else {
     nr = int(uniform(p.row_tkmax[size_t(b) * p.Tq_f + qt]));
     myruns = p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
 #pragma unroll
-    for (int r = 0; r < MAXR; ++r) {
+    for (int r = 0; r < MAXR_Q; ++r) {
       uint2 v = make_uint2(0, 0);
       if (r < nr && qvalid) v = myruns[r];
       rs[r] = v.x;
@@ -477,26 +488,14 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
   }
   const char* lds0 = reinterpret_cast<const char*>(&sKV[0][0][0]);
   constexpr int NQ = 4 * (D / 32);  // dQ MFMAs per tile
-  // dQ^T += K^T dS^T of the tile in stage `st` (K read transposed)
-  auto dq_read = [&](const char* st, int i) {
-    const int kc = i / (D / 32), db = i % (D / 32);
-    const char* t = st + kc * (16 * D * 2);
-    return lds_tr8_at(t + lo.tr[db][0], t + lo.tr[db][1]);
-  };
-  bf16x8 pdb[4];  // previous tile's dS (bf16); zero before the first tile
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) pdb[kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
-  int pbuf = 0;
-  const bool any_tile = have;
   while (have) {
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
     wait_vmem();
-    __syncthreads();
+    __syncthreads();  // every wave is done with the other stage
     if (have) {
-      const int nb = buf == 2 ? 0 : buf + 1;
-      dma.issue(rK, sKV[nb][0], uint32_t(tile) * tile_bytes);
-      dma.issue(rV, sKV[nb][1], uint32_t(tile) * tile_bytes);
+      dma.issue(rK, sKV[buf ^ 1][0], uint32_t(tile) * tile_bytes);
+      dma.issue(rV, sKV[buf ^ 1][1], uint32_t(tile) * tile_bytes);
     }
     const char* cur = lds0 + buf * (2 * TB);
 
@@ -505,7 +504,7 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
     // (lane = query: one lse2 per lane).
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
     {
-      constexpr int NS = D / 8, NM = 2 * NS, G = 4, MPC = NS / 8;
+      constexpr int NS = D / 8, NM = 2 * NS, G = 2, MPC = NS / 8;
       auto rd = [&](int i) {
         const int j = i % NS;
         return lds_b128_at(cur + (i < NS ? 0 : TB) + (j & 1) * (32 * D * 2) + lo.row[j >> 1]);
@@ -547,46 +546,43 @@ __global__ __launch_bounds__(BM * 2, 1) void bwd_dq_kernel(BwdParams p) {
     }
     // partial and ragged tiles: invisible probabilities are zero
     if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid, 0.f);
+      mask_tile<MAXR_Q>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid, 0.f);
 
-    // dS^T = P^T (dP^T - D) of this tile in eight fenced chunks of four
-    // elements, each overlapped with NQ/8 of the previous tile's dQ MFMAs
-    bf16x8 db8[4];
+    // dQ^T += K^T dS^T: dS^T = P^T (dP^T - D) is packed to bf16 one 16-key
+    // chunk at a time, fenced so that each chunk's MFMAs overlap the next
+    // chunk's vector math (K read transposed, two MFMAs ahead).
     {
-      constexpr int G = 4, MPC = NQ / 8;
-      const char* prv = lds0 + pbuf * (2 * TB);
+      constexpr int G = 2, MPK = D / 32;
+      auto rd = [&](int i) {
+        const int kc = i / (D / 32), db = i % (D / 32);
+        const char* t = cur + kc * (16 * D * 2);
+        return lds_tr8_at(t + lo.tr(db, 0), t + lo.tr(db, 1));
+      };
+      bf16x8 db8[4];
       bf16x8 op[NQ];
 #pragma unroll
-      for (int i = 0; i < G; ++i) op[i] = dq_read(prv, i);
+      for (int kc = 0; kc <= 4; ++kc) {
+        if (kc == 0) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int m = 0; m < MPC; ++m) {
-          const int i = c * MPC + m;
-          if (i + G < NQ) op[i + G] = dq_read(prv, i + G);
-          acc[i % (D / 32)] = mfma32(op[i], pdb[i / (D / 32)], acc[i % (D / 32)]);
+          for (int i = 0; i < G; ++i) op[i] = rd(i);
         }
-        const int kb = c >> 2, vg = c & 3;
+        if (kc > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = vg * 4 + e;
-          const float ds = s[kb][v] * (dp[kb][v] - Dq);
-          db8[kb * 2 + (v >> 3)][v & 7] = (__bf16)ds;
+          for (int m = 0; m < MPK; ++m) {
+            const int i = (kc - 1) * MPK + m;
+            if (i + G < NQ) op[i + G] = rd(i + G);
+            acc[m] = mfma32(op[i], db8[kc - 1], acc[m]);
+          }
+        }
+        if (kc < 4) {
+          const int kb = kc >> 1, v0 = (kc & 1) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) db8[kc][e] = (__bf16)(s[kb][v0 + e] * (dp[kb][v0 + e] - Dq));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) pdb[kc] = db8[kc];
-    pbuf = buf;
-    buf = buf == 2 ? 0 : buf + 1;
-  }
-  // the last tile's dQ (its stage is still intact: no copy was issued after it)
-  if (any_tile) {
-    const char* prv = lds0 + pbuf * (2 * TB);
-    mfma_stream<NQ, 4, 2>([&](int i) { return dq_read(prv, i); }, [&](int i, const bf16x8& a) {
-      acc[i % (D / 32)] = mfma32(a, pdb[i / (D / 32)], acc[i % (D / 32)]);
-    });
+    buf ^= 1;
   }
 
   if (qvalid) {

@@ -202,17 +202,22 @@ __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, con
   for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = ((bits >> e) & 1u) ? s[e >> 4][e & 15] : fill;
 }
 
-// Dispatch on the tile's run maximum (wave-uniform).
+// Dispatch on the tile's run maximum (wave-uniform): up to MAXR runs come
+// from registers, more from memory.
 template <int MAXR>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr, const uint32_t* rs,
                                           const uint32_t* rl, const uint2* runs, bool valid, float fill) {
-  static_assert(MAXR == 4, "register copy holds 4 runs");
+  static_assert(MAXR == 2 || MAXR == 4, "register copy holds 2 or 4 runs");
   switch (nr) {
     case 0: mask_runs<0>(s, base, rs, rl, fill); break;
     case 1: mask_runs<1>(s, base, rs, rl, fill); break;
     case 2: mask_runs<2>(s, base, rs, rl, fill); break;
-    case 3: mask_runs<3>(s, base, rs, rl, fill); break;
-    case 4: mask_runs<4>(s, base, rs, rl, fill); break;
+    case 3:
+      if (MAXR >= 3) { mask_runs<(MAXR >= 3 ? 3 : 0)>(s, base, rs, rl, fill); break; }
+      [[fallthrough]];
+    case 4:
+      if (MAXR >= 4) { mask_runs<(MAXR >= 4 ? 4 : 0)>(s, base, rs, rl, fill); break; }
+      [[fallthrough]];
     default: mask_runs_mem(s, base, runs, nr, valid, fill); break;
   }
 }
