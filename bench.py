@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="also time every workload (and the causal comparator) and write one JSON line per run "
                          "to stderr; the stdout line stays the default workload's")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time the ordinary-compare masked-interval kernels against the unsigned-check kernels "
+                         "on every masked workload (one JSON line per pair to stderr)")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the plain copy for counter scaling")
     ap.add_argument("--record-traffic", metavar="DIR", help="write profiles/traffic.json from counter runs in DIR")
     a = ap.parse_args()
@@ -217,11 +220,21 @@ def main():
             for causal in ([False, True] if WORKLOADS[name].mask == "causal" else [False]):
                 line = measure(name, causal, a.steps, a.warmup, cpu=False)
                 print("[bench-all] " + json.dumps(line), file=sys.stderr, flush=True)
+    if a.ablation:
+        for name in WORKLOADS:
+            if WORKLOADS[name].N < 1024:
+                continue
+            base = measure(name, False, a.steps, a.warmup, cpu=False)
+            abl = measure(name, False, a.steps, a.warmup, cpu=False, check=cm.CM_CHECK_ORDINARY_MASKED)
+            rec = {"workload": name, "unsigned_ms": base["ms_per_step"], "ordinary_masked_ms": abl["ms_per_step"],
+                   "reduction": round(1.0 - base["ms_per_step"] / abl["ms_per_step"], 4),
+                   "unsigned_kernel_ms": base["kernel_ms"], "ordinary_masked_kernel_ms": abl["kernel_ms"]}
+            print("[bench-ablation] " + json.dumps(rec), file=sys.stderr, flush=True)
     line = measure(a.workload, a.causal_path, a.steps, a.warmup, cpu=not a.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 
-def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool) -> dict:
+def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool, check: int = 0) -> dict:
     import torch
 
     import runtime_metadata_attention_amd as cm
@@ -238,7 +251,7 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
     spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
     desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev)
     dmd = cm.device_metadata(md, dev)
-    args = cm.attn_args(q, causal=causal_path)
+    args = cm.attn_args(q, causal=causal_path, check=check)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -308,7 +321,8 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         "dtype": "bf16",
         "data": "synthetic (seeded metadata and N(0,1) bf16 tensors)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tiles": list(w.tiles),
-                   "seed": w.seed, "visible_pairs": V, "path": "causal" if causal_path else "descriptor"},
+                   "seed": w.seed, "visible_pairs": V, "path": "causal" if causal_path else "descriptor",
+                   "check": "unsigned" if check == 0 else "ordinary_masked"},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "preprocess_us": round(times["preprocess_kernel"] * 1e3, 2),
         "preprocess_GBps": round(pre_bytes / (times["preprocess_kernel"] * 1e-3) / 1e9, 1),

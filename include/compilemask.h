@@ -122,7 +122,18 @@ typedef struct cm_attn_args {
   int64_t stride_b, stride_h, stride_n;
   float scale;
   int32_t causal;
+  int32_t check;   /* partial-tile visibility check, CM_CHECK_*; 0 = the default */
 } cm_attn_args;
+
+/* Partial-tile visibility checks (cm_attn_args.check).  Both give identical
+ * results; they differ only in the instructions the kernels spend on it.
+ *   CM_CHECK_UNSIGNED: visible runs, one subtraction (hoisted per row) and one
+ *     unsigned compare per run (paper summary, section 3.3.2).
+ *   CM_CHECK_ORDINARY_MASKED: the ablation of section 4.4 / Table 3 there:
+ *     masked intervals (the complement of the visible runs) with two ordinary
+ *     compares and their conjunction per interval.  For measurement only. */
+#define CM_CHECK_UNSIGNED 0
+#define CM_CHECK_ORDINARY_MASKED 1
 
 /* ---- offline: MaskSpec -> symbolic endpoints (section 3.2.2) ------------ */
 

@@ -51,7 +51,11 @@ class cm_metadata(ctypes.Structure):
 class cm_attn_args(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
-                ("scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("check", ctypes.c_int32)]
+
+
+CM_CHECK_UNSIGNED = 0
+CM_CHECK_ORDINARY_MASKED = 1
 
 
 _lib = None
@@ -262,13 +266,14 @@ def cm_build_descriptor(spec: Spec, md: DeviceMetadata, desc: Descriptor, stream
 
 # ------------------------------------------------------------------ attention
 
-def attn_args(q, causal: bool = False, scale: float = 0.0) -> cm_attn_args:
-    """cm_attn_args from a [B, H, N, d] bf16 tensor's shape and strides."""
+def attn_args(q, causal: bool = False, scale: float = 0.0, check: int = CM_CHECK_UNSIGNED) -> cm_attn_args:
+    """cm_attn_args from a [B, H, N, d] bf16 tensor's shape and strides; `check` selects the partial-tile
+    visibility check (CM_CHECK_ORDINARY_MASKED is the ablation kernel)."""
     B, H, N, d = q.shape
     sb, sh, sn, sd = q.stride()
     if sd != 1:
         raise ValueError("the last dimension must be contiguous")
-    return cm_attn_args(B, H, N, d, sb, sh, sn, float(scale), 1 if causal else 0)
+    return cm_attn_args(B, H, N, d, sb, sh, sn, float(scale), 1 if causal else 0, int(check))
 
 
 def _desc_handle(desc):

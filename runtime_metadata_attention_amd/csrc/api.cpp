@@ -122,6 +122,9 @@ cm_status check_attn(const cm_attn_args* args, const cm_desc* desc, AttnDims& di
   if (!std::isfinite(args->scale) || args->scale < 0) return fail(CM_ERR_INVALID, "scale must be finite and >= 0");
   dims.scale = args->scale == 0.f ? 1.0f / std::sqrt(float(args->d)) : args->scale;
   dims.causal = args->causal ? 1 : 0;
+  if (args->check != CM_CHECK_UNSIGNED && args->check != CM_CHECK_ORDINARY_MASKED)
+    return fail(CM_ERR_INVALID, "check must be CM_CHECK_UNSIGNED (0) or CM_CHECK_ORDINARY_MASKED (1)");
+  dims.check = args->check;
   std::memset(&view, 0, sizeof(view));
   if (dims.causal) {
     view.fq = 128; view.fk = 64; view.bk = 128; view.bq = 64;

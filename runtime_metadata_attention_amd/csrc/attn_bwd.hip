@@ -143,7 +143,7 @@ __device__ __forceinline__ bf16x8 lds_tr8_at(const char* p0, const char* p1) {
 
 // ------------------------------------------------------------------ dK / dV
 
-template <int D, int BK, bool CAUSAL>
+template <int D, int BK, bool CAUSAL, int CHK>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = BK / 32;
   static_assert(NW >= 2, "two waves copy lse2 and D");
@@ -199,26 +199,11 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     vreg[c] = as_bf16x8(uv);
   }
 
-  // this key column's visible query-row runs
-  int nr;
-  uint32_t rs[MAXR], rl[MAXR];
-  const uint2* myruns = nullptr;
-  if (CAUSAL) {
-    nr = 1;
-    rs[0] = uint32_t(key); rl[0] = uint32_t(N - key);
-#pragma unroll
-    for (int r = 1; r < MAXR; ++r) { rs[r] = 0; rl[r] = 0; }
-  } else {
-    nr = int(uniform(p.col_tkmax[size_t(b) * p.Tk_b + kt]));
-    myruns = p.col_iv + (size_t(b) * N + (kvalid ? key : 0)) * p.K_c;
-#pragma unroll
-    for (int r = 0; r < MAXR; ++r) {
-      uint2 v = make_uint2(0, 0);
-      if (r < nr && kvalid) v = myruns[r];
-      rs[r] = v.x;
-      rl[r] = v.y - v.x;
-    }
-  }
+  // this key column's visible query-row runs (in registers when at most MAXR)
+  const int nr = CAUSAL ? 1 : int(uniform(p.col_tkmax[size_t(b) * p.Tk_b + kt]));
+  const uint2* myruns = CAUSAL ? nullptr : p.col_iv + (size_t(b) * N + (kvalid ? key : 0)) * p.K_c;
+  const LaneRuns<MAXR> runs =
+      load_runs<MAXR>(CAUSAL, make_uint2(uint32_t(key), uint32_t(N)), myruns, nr, kvalid);
 
   f32x16 adv[D / 32], adk[D / 32];
 #pragma unroll
@@ -320,7 +305,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
     // partial and ragged tiles: invisible probabilities are zero
     if ((cs == 2) || ((ct + 1) * BQ > N))
-      mask_tile<MAXR>(s, uint32_t(ct * BQ + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, kvalid, 0.f);
+      mask_tile<CHK>(s, uint32_t(ct * BQ + 4 * h), nr, runs, myruns, kvalid, 0.f);
 
     // dS = P (dP - D) of this tile and the bf16 P, dS operands, in eight
     // fenced chunks of four elements, each overlapped with 2NC/8 of the
@@ -397,7 +382,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ dQ
 
-template <int D, int BM, bool CAUSAL>
+template <int D, int BM, bool CAUSAL, int CHK>
 __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BM / 32;
   constexpr int TILE = BN * D;
@@ -442,25 +427,10 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
   const float lse2 = qvalid ? p.lse2[rbase + q] : INFINITY;
   const float Dq = qvalid ? p.D[rbase + q] : 0.f;
 
-  int nr;
-  uint32_t rs[MAXR_Q], rl[MAXR_Q];
-  const uint2* myruns = nullptr;
-  if (CAUSAL) {
-    nr = 1;
-    rs[0] = 0; rl[0] = uint32_t(q + 1);
-#pragma unroll
-    for (int r = 1; r < MAXR_Q; ++r) { rs[r] = 0; rl[r] = 0; }
-  } else {
-    nr = int(uniform(p.row_tkmax[size_t(b) * p.Tq_f + qt]));
-    myruns = p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
-#pragma unroll
-    for (int r = 0; r < MAXR_Q; ++r) {
-      uint2 v = make_uint2(0, 0);
-      if (r < nr && qvalid) v = myruns[r];
-      rs[r] = v.x;
-      rl[r] = v.y - v.x;
-    }
-  }
+  const int nr = CAUSAL ? 1 : int(uniform(p.row_tkmax[size_t(b) * p.Tq_f + qt]));
+  const uint2* myruns = CAUSAL ? nullptr : p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+  const LaneRuns<MAXR_Q> runs =
+      load_runs<MAXR_Q>(CAUSAL, make_uint2(0u, uint32_t(q + 1)), myruns, nr, qvalid);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -546,7 +516,7 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
     }
     // partial and ragged tiles: invisible probabilities are zero
     if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<MAXR_Q>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid, 0.f);
+      mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, 0.f);
 
     // dQ^T += K^T dS^T: dS^T = P^T (dP^T - D) is packed to bf16 one 16-key
     // chunk at a time, fenced so that each chunk's MFMAs overlap the next
@@ -653,11 +623,16 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dvv);
   dim3 grid(p.Tk_b * a.H * a.B);
-  const bool c = a.causal != 0;
-#define CM_DKDV(DD, BKK)                                                                              \
-  do {                                                                                               \
-    if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true>), grid, dim3(BKK * 2), 0, stream, p);  \
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false>), grid, dim3(BKK * 2), 0, stream, p);   \
+  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked;
+#define CM_DKDV(DD, BKK)                                                                                              \
+  do {                                                                                                               \
+    if (o) {                                                                                                         \
+      if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
+    } else {                                                                                                         \
+      if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckUnsigned>), grid, dim3(BKK * 2), 0, stream, p); \
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckUnsigned>), grid, dim3(BKK * 2), 0, stream, p); \
+    }                                                                                                                \
   } while (0)
   if (a.d == 128) { if (dv.bk == 128) CM_DKDV(128, 128); else CM_DKDV(128, 64); }
   else { if (dv.bk == 128) CM_DKDV(64, 128); else CM_DKDV(64, 64); }
@@ -677,11 +652,16 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
   p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dq = static_cast<uint16_t*>(dq);
   dim3 grid(p.Tq_f * a.H * a.B);
-  const bool c = a.causal != 0;
-#define CM_DQ(DD, BMM)                                                                             \
-  do {                                                                                            \
-    if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true>), grid, dim3(BMM * 2), 0, stream, p); \
-    else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false>), grid, dim3(BMM * 2), 0, stream, p);  \
+  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked;
+#define CM_DQ(DD, BMM)                                                                                              \
+  do {                                                                                                             \
+    if (o) {                                                                                                       \
+      if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
+      else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
+    } else {                                                                                                       \
+      if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckUnsigned>), grid, dim3(BMM * 2), 0, stream, p); \
+      else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckUnsigned>), grid, dim3(BMM * 2), 0, stream, p); \
+    }                                                                                                              \
   } while (0)
   if (a.d == 128) { if (dv.fq == 128) CM_DQ(128, 128); else CM_DQ(128, 64); }
   else { if (dv.fq == 128) CM_DQ(64, 128); else CM_DQ(64, 64); }

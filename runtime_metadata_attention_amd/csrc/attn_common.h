@@ -164,39 +164,107 @@ __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
   return uint32_t(blk * 32 + (v >> 2) * 8 + (v & 3));
 }
 
-// Partial-tile visibility (unsigned endpoint compares) for a score tile of two
-// 32-blocks: element e is visible when (base + offset(e) - start_r) <u len_r
-// for some run r; invisible elements become `fill` (-inf for scores before a
-// softmax, 0 for probabilities).  `base` is the tile's first index plus 4h.
-// NR runs are held in registers.
-template <int NR>
-__device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const uint32_t* rs, const uint32_t* rl,
-                                          float fill) {
-  uint32_t off[NR > 0 ? NR : 1];
+// Partial-tile visibility checks.  A lane's interval data are loop-invariant
+// registers (LaneRuns); `base` is the tile's first index plus 4h, so element
+// e of the tile sits at index j = base + elem_offset(e).
+//   kCheckUnsigned: the visible runs as (start, length); j is visible when
+//     (j - start) <u length for some run: one subtraction (hoisted) and one
+//     compare per run (CompileMask paper summary, section 3.3.2).
+//   kCheckOrdinaryMasked: the ablation the paper summary compares against
+//     (section 4.4, Table 3): the complement of the visible runs as masked
+//     intervals [lo, hi), and j is masked when lo <= j and j < hi for some
+//     interval: two compares and their conjunction per interval.
+// Invisible elements become `fill` (-inf for scores before a softmax, 0 for
+// probabilities).
+constexpr int kCheckUnsigned = 0;
+constexpr int kCheckOrdinaryMasked = 1;
+
+// A lane's first MAXR visible runs as (start, length); absent runs are
+// (0, 0) and only follow present ones.
+template <int MAXR>
+struct LaneRuns {
+  uint32_t a[MAXR], b[MAXR];
+};
+
+// Check against the first NR runs held in registers (NR <= MAXR; every run
+// of the tile's rows or columns is among them).
+template <int NR, int CHK, int MAXR>
+__device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const LaneRuns<MAXR>& lr, float fill) {
+  if (CHK == kCheckUnsigned) {
+    uint32_t off[NR > 0 ? NR : 1];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) off[r] = base - rs[r];
+    for (int r = 0; r < NR; ++r) off[r] = base - lr.a[r];
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      bool vis = false;
+      for (int v = 0; v < 16; ++v) {
+        bool vis = false;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) vis = vis | (off[r] + elem_offset(blk, v) < rl[r]);
-      s[blk][v] = vis ? s[blk][v] : fill;
+        for (int r = 0; r < NR; ++r) vis = vis | (off[r] + elem_offset(blk, v) < lr.b[r]);
+        s[blk][v] = vis ? s[blk][v] : fill;
+      }
+    }
+  } else {
+    // the masked intervals: before each present run, and after the last one
+    // (formed here, per tile: the empty asm keeps the compiler from hoisting
+    // them, and everything derived from them, out of the tile loop)
+    uint32_t lo[NR + 1], hi[NR + 1], prev = 0;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      uint32_t st = lr.a[r], len = lr.b[r];
+      asm volatile("" : "+v"(st), "+v"(len));
+      const bool present = len > 0;
+      lo[r] = present ? prev : 0u;
+      hi[r] = present ? st : 0u;
+      prev = present ? st + len : prev;
+    }
+    lo[NR] = prev;
+    hi[NR] = 0xFFFFFFFFu;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t j = base + elem_offset(blk, v);
+        bool masked = false;
+#pragma unroll
+        for (int k = 0; k <= NR; ++k) masked = masked || ((j >= lo[k]) && (j < hi[k]));
+        s[blk][v] = masked ? fill : s[blk][v];
+      }
     }
   }
 }
 
 // Same check with the runs read from memory (rows or columns with more runs
 // than the register copy holds).
+template <int CHK>
 __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, const uint2* runs, int nr, bool valid,
                                               float fill) {
   uint32_t bits = 0;
-  for (int r = 0; r < nr; ++r) {
-    const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
-    const uint32_t off = base - rr.x, len = rr.y - rr.x;
+  if (CHK == kCheckUnsigned) {
+    for (int r = 0; r < nr; ++r) {
+      const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
+      const uint32_t off = base - rr.x, len = rr.y - rr.x;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) bits |= uint32_t(off + elem_offset(e >> 4, e & 15) < len) << e;
+      for (int e = 0; e < 32; ++e) bits |= uint32_t(off + elem_offset(e >> 4, e & 15) < len) << e;
+    }
+  } else {
+    uint32_t masked = 0, prev = 0;
+    for (int r = 0; r < nr; ++r) {
+      const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
+      if (rr.y > rr.x) {
+        uint32_t jb = base;
+        asm volatile("" : "+v"(jb));  // indices formed per run, not hoisted
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const uint32_t j = jb + elem_offset(e >> 4, e & 15);
+          masked |= uint32_t((j >= prev) && (j < rr.x)) << e;
+        }
+        prev = rr.y;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) masked |= uint32_t(base + elem_offset(e >> 4, e & 15) >= prev) << e;
+    bits = ~masked;
   }
 #pragma unroll
   for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = ((bits >> e) & 1u) ? s[e >> 4][e & 15] : fill;
@@ -204,22 +272,42 @@ __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, con
 
 // Dispatch on the tile's run maximum (wave-uniform): up to MAXR runs come
 // from registers, more from memory.
-template <int MAXR>
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr, const uint32_t* rs,
-                                          const uint32_t* rl, const uint2* runs, bool valid, float fill) {
-  static_assert(MAXR == 2 || MAXR == 4, "register copy holds 2 or 4 runs");
+template <int CHK, int MAXR>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr, const LaneRuns<MAXR>& lr,
+                                          const uint2* runs, bool valid, float fill) {
+  static_assert(MAXR == 1 || MAXR == 2 || MAXR == 4, "register copy holds 1, 2 or 4 runs");
   switch (nr) {
-    case 0: mask_runs<0>(s, base, rs, rl, fill); break;
-    case 1: mask_runs<1>(s, base, rs, rl, fill); break;
-    case 2: mask_runs<2>(s, base, rs, rl, fill); break;
+    case 0: mask_runs<0, CHK>(s, base, lr, fill); break;
+    case 1: mask_runs<1, CHK>(s, base, lr, fill); break;
+    case 2:
+      if (MAXR >= 2) { mask_runs<(MAXR >= 2 ? 2 : 0), CHK>(s, base, lr, fill); break; }
+      [[fallthrough]];
     case 3:
-      if (MAXR >= 3) { mask_runs<(MAXR >= 3 ? 3 : 0)>(s, base, rs, rl, fill); break; }
+      if (MAXR >= 3) { mask_runs<(MAXR >= 3 ? 3 : 0), CHK>(s, base, lr, fill); break; }
       [[fallthrough]];
     case 4:
-      if (MAXR >= 4) { mask_runs<(MAXR >= 4 ? 4 : 0)>(s, base, rs, rl, fill); break; }
+      if (MAXR >= 4) { mask_runs<(MAXR >= 4 ? 4 : 0), CHK>(s, base, lr, fill); break; }
       [[fallthrough]];
-    default: mask_runs_mem(s, base, runs, nr, valid, fill); break;
+    default: mask_runs_mem<CHK>(s, base, runs, nr, valid, fill); break;
   }
+}
+
+// The lane's first MAXR runs from its interval-table row (the first `nr`
+// entries, nr being the tile's run maximum) or, on the maskless causal path,
+// the single run given as [start, end).
+template <int MAXR>
+__device__ __forceinline__ LaneRuns<MAXR> load_runs(bool causal, uint2 causal_run, const uint2* row, int nr,
+                                                    bool valid) {
+  LaneRuns<MAXR> lr;
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    uint2 v = make_uint2(0u, 0u);
+    if (causal) { if (r == 0) v = causal_run; }
+    else if (r < nr && valid) v = row[r];
+    lr.a[r] = v.x;
+    lr.b[r] = v.y - v.x;
+  }
+  return lr;
 }
 
 // XCD-aware work-group order.  MI355X deals consecutive work-group ids

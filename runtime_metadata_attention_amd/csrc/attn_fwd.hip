@@ -45,7 +45,7 @@ struct FwdParams {
 constexpr int BN = 64;
 constexpr int MAXR = 4;  // runs kept in registers; more are read from memory
 
-template <int D, int BM, bool CAUSAL>
+template <int D, int BM, bool CAUSAL, int CHK>
 __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int NW = BM / 32;
   // K and V tiles, double-buffered, swizzled (see swz())
@@ -79,26 +79,10 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     qreg[c] = as_bf16x8(u);
   }
 
-  // this row's visible runs: start and length
-  int nr;
-  uint32_t rs[MAXR], rl[MAXR];
-  const uint2* myruns = nullptr;
-  if (CAUSAL) {
-    nr = 1;
-    rs[0] = 0; rl[0] = uint32_t(q + 1);
-#pragma unroll
-    for (int r = 1; r < MAXR; ++r) { rs[r] = 0; rl[r] = 0; }
-  } else {
-    nr = int(uniform(p.row_tkmax[size_t(b) * p.Tq + qt]));
-    myruns = p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
-#pragma unroll
-    for (int r = 0; r < MAXR; ++r) {
-      uint2 v = make_uint2(0, 0);
-      if (r < nr && qvalid) v = myruns[r];
-      rs[r] = v.x;
-      rl[r] = v.y - v.x;
-    }
-  }
+  // this row's visible runs (in registers when there are at most MAXR)
+  const int nr = CAUSAL ? 1 : int(uniform(p.row_tkmax[size_t(b) * p.Tq + qt]));
+  const uint2* myruns = CAUSAL ? nullptr : p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+  const LaneRuns<MAXR> runs = load_runs<MAXR>(CAUSAL, make_uint2(0u, uint32_t(q + 1)), myruns, nr, qvalid);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -146,7 +130,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
     // partial tiles (and a ragged last tile): unsigned endpoint checks
     if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<MAXR>(s, uint32_t(ct * BN + 4 * h), CAUSAL ? 1 : nr, rs, rl, myruns, qvalid, -INFINITY);
+      mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, -INFINITY);
 
     // online softmax in the log2 domain, scale folded into the exponent.  The
     // running max is only moved (and O rescaled) when some row's max grew by
@@ -216,11 +200,18 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BM, bool CAUSAL>
+template <int D, int BM, bool CAUSAL, int CHK>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   dim3 grid(p.Tq * p.H * p.B);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BM, CAUSAL>), grid, dim3(BM * 2), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BM, CAUSAL, CHK>), grid, dim3(BM * 2), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int BM>
+hipError_t launch_dc(const FwdParams& p, bool causal, int check, hipStream_t stream) {
+  if (check == kCheckOrdinaryMasked)
+    return causal ? launch<D, BM, true, kCheckOrdinaryMasked>(p, stream) : launch<D, BM, false, kCheckOrdinaryMasked>(p, stream);
+  return causal ? launch<D, BM, true, kCheckUnsigned>(p, stream) : launch<D, BM, false, kCheckUnsigned>(p, stream);
 }
 
 }  // namespace
@@ -246,12 +237,8 @@ hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, cons
   p.fbm = dv.fbm; p.Wf = dv.Wf; p.row_iv = reinterpret_cast<const uint2*>(dv.row_iv); p.K_r = dv.K_r;
   p.row_tkmax = dv.row_tkmax;
   const bool c = a.causal != 0;
-  if (a.d == 128) {
-    if (dv.fq == 128) return c ? launch<128, 128, true>(p, stream) : launch<128, 128, false>(p, stream);
-    return c ? launch<128, 64, true>(p, stream) : launch<128, 64, false>(p, stream);
-  }
-  if (dv.fq == 128) return c ? launch<64, 128, true>(p, stream) : launch<64, 128, false>(p, stream);
-  return c ? launch<64, 64, true>(p, stream) : launch<64, 64, false>(p, stream);
+  if (a.d == 128) return dv.fq == 128 ? launch_dc<128, 128>(p, c, a.check, stream) : launch_dc<128, 64>(p, c, a.check, stream);
+  return dv.fq == 128 ? launch_dc<64, 128>(p, c, a.check, stream) : launch_dc<64, 64>(p, c, a.check, stream);
 }
 
 }  // namespace cm

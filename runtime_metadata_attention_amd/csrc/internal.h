@@ -67,6 +67,7 @@ struct AttnDims {
   int64_t sb, sh, sn;            // element strides of the bf16 tensors
   float scale;
   int32_t causal;
+  int32_t check;                 // partial-tile check: 0 unsigned visible runs, 1 ordinary masked intervals
 };
 struct DescView {                // device pointers into a descriptor
   const uint32_t* fbm;

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 ATOL, RL2, LSE_ATOL = 2e-2, 1e-2, 1e-3
 
 
-def run_gpu(spec_text, md, t, tiles, causal=False, desc=None, spec=None):
+def run_gpu(spec_text, md, t, tiles, causal=False, desc=None, spec=None, check=cm.CM_CHECK_UNSIGNED):
     """Build the descriptor (unless causal) and run forward + backward."""
     q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
     B, H, N, d = q.shape
@@ -33,7 +33,7 @@ def run_gpu(spec_text, md, t, tiles, causal=False, desc=None, spec=None):
         spec = spec or cm.cm_spec_compile(spec_text)
         desc = desc or cm.Descriptor(spec, B, N, md.seg_cap, tiles)
         cm.cm_build_descriptor(spec, cm.device_metadata(md), desc)
-    args = cm.attn_args(q, causal=causal)
+    args = cm.attn_args(q, causal=causal, check=check)
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
     cm.cm_attn_fwd(args, q, k, v, None if causal else desc, o, lse)
@@ -124,6 +124,56 @@ def test_causal_descriptor_path_equals_maskless_path_bitwise():
     for n in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[n], b[n]), n
     check_all(b, t, "causal", md)
+
+
+def many_column_runs_md(N=640):
+    """Retrieval metadata whose first segment is referenced by every other
+    later segment, so its key columns carry more runs than the kernels hold
+    in registers."""
+    L = 40
+    bounds = list(range(L, N + 1, L))
+    n = len(bounds) - 1
+    refs = [[]] + [[0] if i % 2 == 0 else [max(0, i - 1)] for i in range(1, n)]
+    return metadata_from_segments(N, n + 1, 2, ("g",), [{"scalars": [L], "bounds": bounds, "refs": refs}])
+
+
+ABLATION = [
+    # mask, N, d, tiles, seed
+    ("hstu", 517, 128, (128, 64, 128, 64), 12),
+    ("shared_prompt", 333, 64, (64, 64, 64, 64), 15),
+    ("retrieval", 777, 128, (128, 64, 128, 64), 14),
+    ("many_runs", 640, 128, (128, 64, 128, 64), 18),
+]
+
+
+@pytest.mark.parametrize("mask,N,d,tiles,seed", ABLATION)
+def test_ordinary_masked_check_equals_unsigned_check_bitwise(mask, N, d, tiles, seed):
+    """The ablation kernels (ordinary compares on masked intervals) decide the
+    same visibility as the unsigned-check kernels, so every output is equal."""
+    print(f"[ablation] {mask} N={N} d={d} tiles={tiles}", flush=True)
+    if mask == "many_runs":
+        md, mask = many_column_runs_md(N), "retrieval"
+        m = om.dense_mask(mask, md, 0).astype(np.int8)
+        starts = np.diff(np.vstack([np.zeros((1, N), np.int8), m]), axis=0) == 1
+        assert starts.sum(axis=0).max() > 4, "the case must exceed the register copy of column runs"
+    else:
+        md = small_md(mask, N=N, seed=seed, B=2)
+    t = make_tensors(md.B, 2, N, d, seed)
+    a = run_gpu(specs.BY_MASK[mask], md, t, tiles)
+    b = run_gpu(specs.BY_MASK[mask], md, t, tiles, check=cm.CM_CHECK_ORDINARY_MASKED)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+    check_all(b, t, mask, md)
+
+
+def test_ordinary_masked_check_on_the_causal_path():
+    N = 700
+    md = small_md("causal", N=N, B=1)
+    t = make_tensors(1, 2, N, 128, 32)
+    a = run_gpu(None, md, t, None, causal=True)
+    b = run_gpu(None, md, t, None, causal=True, check=cm.CM_CHECK_ORDINARY_MASKED)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
 
 
 def test_strided_layout_matches_contiguous():

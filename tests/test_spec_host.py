@@ -183,4 +183,7 @@ def test_argument_checks_without_gpu():
     args = cm.cm_attn_args(1, 1, 128, 64, 0, 0, 0, 0.0, 0)
     st = cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None)
     assert st == -1  # non-causal needs a descriptor
+    args = cm.cm_attn_args(1, 1, 128, 64, 0, 0, 0, 0.0, 1, 2)
+    st = cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None)
+    assert st == -2  # no such partial-tile check
     assert cm.cm_status_str(-4) == "descriptor/spec/argument mismatch"
