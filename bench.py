@@ -243,13 +243,14 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
 
     w = WORKLOADS[workload]
     md = make_metadata(w)
-    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} tiles={w.tiles}")
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} tiles={w.tiles}"
+        + (f" packed samples={md.B}" if w.packed else ""))
     t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
     dev = torch.device("cuda", 0)
     q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
     del t
     spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
-    desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev)
+    desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev, packed=md.B if w.packed else 0)
     dmd = cm.device_metadata(md, dev)
     args = cm.attn_args(q, causal=causal_path, check=check)
     o = torch.empty_like(q)
@@ -322,6 +323,7 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         "data": "synthetic (seeded metadata and N(0,1) bf16 tensors)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tiles": list(w.tiles),
                    "seed": w.seed, "visible_pairs": V, "path": "causal" if causal_path else "descriptor",
+                   "packed_samples": int(md.B) if w.packed else 0,
                    "check": "unsigned" if check == 0 else "ordinary_masked"},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "preprocess_us": round(times["preprocess_kernel"] * 1e3, 2),

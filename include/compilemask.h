@@ -81,6 +81,8 @@ typedef enum cm_status {
 #define CM_MD_BOUNDS_ORDER 2u  /* a used boundary is smaller than the one before */
 #define CM_MD_BOUNDS_RANGE 4u  /* a used boundary lies outside [0, N]          */
 #define CM_MD_REF_RANGE 8u     /* a used reference lies outside [-1, n_seg)    */
+#define CM_MD_CU_SEQLENS 16u   /* packed batch: cu_seqlens is not 0 = c[0] <= c[1]
+                                  <= ... <= c[n] = total length                 */
 
 #define CM_DESC_MAGIC 0x31444D43u
 
@@ -100,8 +102,13 @@ typedef struct cm_tiles {
  *                              [seg_bounds[b][s], seg_bounds[b][s+1]), s < n_seg[b]
  *   n_seg      [B]
  *   refs       [B][seg_cap][n_refs]  referenced segment ids, -1 = none
+ *   cu_seqlens [B+1]           packed batches only (else NULL): sample b holds
+ *                              tokens [cu_seqlens[b], cu_seqlens[b+1]) of one
+ *                              packed sequence
  * A pointer may be NULL when its array is empty (n_scalars == 0, seg_cap == 0
- * or n_refs == 0). */
+ * or n_refs == 0).  In a packed batch every sample's scalars and boundaries
+ * are in the sample's own coordinates (its first token is 0 and its length
+ * plays the part of N). */
 typedef struct cm_metadata {
   const int32_t* scalars;
   const int32_t* seg_bounds;
@@ -109,6 +116,7 @@ typedef struct cm_metadata {
   const int32_t* refs;
   int32_t n_scalars;
   int32_t n_refs;
+  const int32_t* cu_seqlens;
 } cm_metadata;
 
 /* Attention shapes.  q, k, v, o, dO, dq, dk, dv are bf16 [B][H][N][d] with
@@ -184,6 +192,20 @@ cm_status cm_desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_ca
                        const cm_tiles* tiles, void* dev_buf, size_t bytes, cm_desc** out);
 void cm_desc_free(cm_desc* desc);
 
+/* Packed variable-length batches (cu_seqlens style).  n_samples sequences
+ * are laid end to end as one sequence of T tokens; a token attends only to
+ * its own sample's keys, under the spec's rules in the sample's coordinates.
+ * The descriptor covers that one sequence (its header has B = 1, N = T and
+ * word 15 = n_samples; sample_err has n_samples words), so attention runs
+ * with cm_attn_args B = 1, N = T on [1][H][T][d] tensors (or [T][H][d] via
+ * the strides); tiles that straddle two samples are partial.  Build it with
+ * cm_build_descriptor and metadata whose cu_seqlens is set.  Same ownership
+ * and errors as cm_desc_size / cm_desc_init. */
+cm_status cm_desc_size_packed(const cm_spec* spec, int32_t n_samples, int32_t T, int32_t seg_cap,
+                              const cm_tiles* tiles, size_t* bytes);
+cm_status cm_desc_init_packed(const cm_spec* spec, int32_t n_samples, int32_t T, int32_t seg_cap,
+                              const cm_tiles* tiles, void* dev_buf, size_t bytes, cm_desc** out);
+
 /* Byte offsets of the descriptor sections, in layout order: header,
  * sample_err, row_tkmax, col_tkmax, fbm, bbm, row_iv, col_iv; then the
  * total size.  offsets must hold 9 entries. */
@@ -194,7 +216,8 @@ cm_status cm_desc_offsets(const cm_desc* desc, size_t* offsets);
 /* One preprocess kernel launch: evaluate the compiled endpoints of `spec`
  * against `md` and write the whole descriptor (header, both interval tables,
  * both bitmaps, per-tile run maxima, error words).  desc must come from
- * cm_desc_init with the same spec.  Asynchronous on `stream`. */
+ * cm_desc_init (md->cu_seqlens NULL) or cm_desc_init_packed (md->cu_seqlens
+ * set) with the same spec.  Asynchronous on `stream`. */
 cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_desc* desc,
                               cm_stream stream);
 

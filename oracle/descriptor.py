@@ -22,8 +22,9 @@ Readings where the pages are silent (each is frozen here and in the library):
 Byte layout (all uint32, each section starting at a multiple of 256 bytes,
 gaps zero):
   header[16]   magic 0x31444D43, B, N, K_r, K_c, fwd_q, fwd_k, bwd_k, bwd_q,
-               Tq_f, Tk_f, Tk_b, Tq_b, err_or, seg_cap, 0
-  sample_err[B]
+               Tq_f, Tk_f, Tk_b, Tq_b, err_or, seg_cap, n_samples (packed
+               batches; 0 otherwise)
+  sample_err[B]                 (packed batch: [n_samples])
   row_tkmax[B][Tq_f]
   col_tkmax[B][Tk_b]
   fbm[B][Tq_f][ceil(Tk_f/16)]   forward grid: query tiles x key tiles
@@ -47,15 +48,16 @@ def _align(x: int, a: int = 256) -> int:
     return (x + a - 1) // a * a
 
 
-def layout(B: int, N: int, K_r: int, K_c: int, tiles):
-    """Byte offsets of each section and the total size."""
+def layout(B: int, N: int, K_r: int, K_c: int, tiles, n_err: int = None):
+    """Byte offsets of each section and the total size (n_err sample-error
+    words: B, or the sample count of a packed batch)."""
     fq, fk, bk, bq = tiles
     Tq_f, Tk_f = math.ceil(N / fq), math.ceil(N / fk)
     Tk_b, Tq_b = math.ceil(N / bk), math.ceil(N / bq)
     Wf, Wb = math.ceil(Tk_f / 16), math.ceil(Tq_b / 16)
     sizes = [
         ("header", 16 * 4),
-        ("sample_err", B * 4),
+        ("sample_err", (B if n_err is None else n_err) * 4),
         ("row_tkmax", B * Tq_f * 4),
         ("col_tkmax", B * Tk_b * 4),
         ("fbm", B * Tq_f * Wf * 4),
@@ -138,7 +140,10 @@ def sample_tables(mask: str, md, b: int, tiles, block_rows: int = 1024):
     prev = np.zeros(N, bool)
     for r0 in range(0, N, block):
         r1 = min(N, r0 + block)
-        M = _masks.visible(mask, md, b, np.arange(r0, r1), cols)
+        if _masks.is_packed(md):
+            M = _masks.packed_visible(mask, md, np.arange(r0, r1), cols)
+        else:
+            M = _masks.visible(mask, md, b, np.arange(r0, r1), cols)
         row_runs.extend(runs_of_rows(M))
         # column runs: a run starts where a column turns visible going down
         # the rows and ends where it turns invisible
@@ -171,9 +176,14 @@ def sample_tables(mask: str, md, b: int, tiles, block_rows: int = 1024):
 
 
 def build(mask: str, md, K_r: int, K_c: int, tiles, block_rows: int = 1024) -> np.ndarray:
-    """The whole descriptor as a uint32 array (bytes / 4 words)."""
-    B, N = md.B, md.N
-    off, total, dims = layout(B, N, K_r, K_c, tiles)
+    """The whole descriptor as a uint32 array (bytes / 4 words).  A packed
+    batch (md.cu_seqlens set) gives the descriptor of its one sequence:
+    B = 1, N = the total length, header word 15 = the sample count and one
+    error word per sample."""
+    packed = _masks.is_packed(md)
+    n_samples = len(md.cu_seqlens) - 1 if packed else 0
+    B, N = (1, md.N) if packed else (md.B, md.N)
+    off, total, dims = layout(B, N, K_r, K_c, tiles, n_samples if packed else None)
     fq, fk, bk, bq = tiles
     words = np.zeros(total // 4, np.uint32)
 
@@ -182,12 +192,12 @@ def build(mask: str, md, K_r: int, K_c: int, tiles, block_rows: int = 1024) -> n
         vals = np.asarray(values, np.uint32).ravel()
         words[base: base + len(vals)] = vals
 
-    errs = [_masks.validate(md, b) for b in range(B)]
+    errs = _masks.packed_errors(md) if packed else [_masks.validate(md, b) for b in range(B)]
     err_or = 0
     for e in errs:
         err_or |= e
     put("header", 0, [MAGIC, B, N, K_r, K_c, fq, fk, bk, bq,
-                      dims["Tq_f"], dims["Tk_f"], dims["Tk_b"], dims["Tq_b"], err_or, md.seg_cap, 0])
+                      dims["Tq_f"], dims["Tk_f"], dims["Tk_b"], dims["Tq_b"], err_or, md.seg_cap, n_samples])
     put("sample_err", 0, errs)
     Tq_f, Tk_f, Tk_b, Tq_b, Wf, Wb = (dims[k] for k in ("Tq_f", "Tk_f", "Tk_b", "Tq_b", "Wf", "Wb"))
     for b in range(B):
@@ -223,14 +233,14 @@ def build(mask: str, md, K_r: int, K_c: int, tiles, block_rows: int = 1024) -> n
 class View:
     """Named, shaped views into a descriptor word array (either side's)."""
 
-    def __init__(self, words: np.ndarray, B: int, N: int, K_r: int, K_c: int, tiles):
+    def __init__(self, words: np.ndarray, B: int, N: int, K_r: int, K_c: int, tiles, n_err: int = None):
         self.words = np.asarray(words, np.uint32)
-        self.off, self.total, self.dims = layout(B, N, K_r, K_c, tiles)
+        self.off, self.total, self.dims = layout(B, N, K_r, K_c, tiles, n_err)
         d = self.dims
         self.B, self.N, self.K_r, self.K_c = B, N, K_r, K_c
         self.shapes = {
             "header": (16,),
-            "sample_err": (B,),
+            "sample_err": (B if n_err is None else n_err,),
             "row_tkmax": (B, d["Tq_f"]),
             "col_tkmax": (B, d["Tk_b"]),
             "fbm": (B, d["Tq_f"], d["Wf"]),

@@ -22,6 +22,7 @@ ERR_NSEG = 1          # n_seg outside [0, seg_cap]
 ERR_BOUNDS_ORDER = 2  # segment boundaries decrease somewhere
 ERR_BOUNDS_RANGE = 4  # a used boundary lies outside [0, N]
 ERR_REF_RANGE = 8     # a used reference lies outside [-1, n_seg)
+ERR_CU_SEQLENS = 16   # packed batch: cu_seqlens does not run 0 <= ... <= N without decreasing
 
 MASKS = ("causal", "shared_prompt", "hstu", "retrieval", "full", "none")
 
@@ -111,17 +112,81 @@ def visible(mask: str, md, b: int, rows: np.ndarray, cols: np.ndarray) -> np.nda
     raise KeyError(mask)
 
 
+# ---------------------------------------------------------------- packed batches
+#
+# A packed batch lays its samples end to end as one sequence of md.N tokens;
+# md.cu_seqlens[b] is the first token of sample b and cu_seqlens[-1] = N.
+# Token i of sample b sees key j exactly when j belongs to the same sample and
+# the sample's own rule (evaluated in its coordinates, with its length as N)
+# lets local row i - c_b see local key j - c_b.
+
+
+def cu_valid(md) -> bool:
+    cu = [int(x) for x in md.cu_seqlens]
+    return cu[0] == 0 and cu[-1] == md.N and all(a <= b for a, b in zip(cu, cu[1:]))
+
+
+def sample_md(md, b: int):
+    """Sample b of a packed batch as a one-sample metadata of its own length."""
+    cu = md.cu_seqlens
+    out = md.copy()
+    out.B = 1
+    out.N = int(cu[b + 1]) - int(cu[b])
+    out.scalars = md.scalars[b: b + 1].copy()
+    out.seg_bounds = md.seg_bounds[b: b + 1].copy()
+    out.n_seg = md.n_seg[b: b + 1].copy()
+    out.refs = md.refs[b: b + 1].copy()
+    out.cu_seqlens = None
+    return out
+
+
+def packed_errors(md):
+    """Error word of every sample of a packed batch."""
+    n = len(md.cu_seqlens) - 1
+    if not cu_valid(md):
+        return [ERR_CU_SEQLENS] * n
+    return [validate(sample_md(md, b), 0) for b in range(n)]
+
+
+def packed_visible(mask: str, md, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Dense visibility of a packed batch for global rows x global columns."""
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    out = np.zeros((len(rows), len(cols)), bool)
+    if not cu_valid(md):
+        return out
+    cu = [int(x) for x in md.cu_seqlens]
+    for b in range(len(cu) - 1):
+        c0, c1 = cu[b], cu[b + 1]
+        rsel = np.nonzero((rows >= c0) & (rows < c1))[0]
+        csel = np.nonzero((cols >= c0) & (cols < c1))[0]
+        if len(rsel) == 0 or len(csel) == 0:
+            continue
+        sub = visible(mask, sample_md(md, b), 0, rows[rsel] - c0, cols[csel] - c0)
+        out[np.ix_(rsel, csel)] = sub
+    return out
+
+
+def is_packed(md) -> bool:
+    return getattr(md, "cu_seqlens", None) is not None
+
+
 def dense_mask(mask: str, md, b: int) -> np.ndarray:
     """Full N x N boolean mask of sample b (small N only)."""
     ar = np.arange(md.N)
+    if is_packed(md):
+        return packed_visible(mask, md, ar, ar)
     return visible(mask, md, b, ar, ar)
 
 
 def row_block_fn(mask: str, md):
-    """Callback (b, r0, r1) -> bool[r1 - r0, N] for the attention oracle."""
+    """Callback (b, r0, r1) -> bool[r1 - r0, N] for the attention oracle (a
+    packed batch is one sequence: b is then 0)."""
     cols = np.arange(md.N)
 
     def fn(b, r0, r1):
+        if is_packed(md):
+            return packed_visible(mask, md, np.arange(r0, r1), cols)
         return visible(mask, md, b, np.arange(r0, r1), cols)
 
     return fn

@@ -8,6 +8,8 @@ library itself must be built: there is no fallback of any kind.
 
     spec = cm_spec_compile(text)
     desc = Descriptor(spec, B, N, seg_cap, tiles, device)     # cm_desc_size + cm_desc_init
+    # packed batches: Descriptor(spec, 1, T, seg_cap, tiles, device, packed=n_samples)
+    # with metadata carrying cu_seqlens
     cm_build_descriptor(spec, device_metadata(md, device), desc)
     cm_attn_fwd(attn_args(q), q, k, v, desc, o, lse)
     cm_attn_bwd(attn_args(q), q, k, v, o, lse, do, desc, dq, dk, dv, ws)
@@ -27,7 +29,8 @@ STATUS = {0: "CM_OK", -1: "CM_ERR_NULL", -2: "CM_ERR_INVALID", -3: "CM_ERR_PARSE
 SECTIONS = ("header", "sample_err", "row_tkmax", "col_tkmax", "fbm", "bbm", "row_iv", "col_iv", "total")
 # every symbol include/compilemask.h declares
 EXPORTS = ("cm_spec_compile", "cm_spec_free", "cm_spec_info", "cm_spec_dump", "cm_spec_eval_host",
-           "cm_desc_size", "cm_desc_init", "cm_desc_free", "cm_desc_offsets", "cm_build_descriptor",
+           "cm_desc_size", "cm_desc_init", "cm_desc_size_packed", "cm_desc_init_packed", "cm_desc_free",
+           "cm_desc_offsets", "cm_build_descriptor",
            "cm_attn_fwd", "cm_attn_bwd_workspace", "cm_attn_bwd", "cm_attn_bwd_stage",
            "cm_status_str", "cm_last_error", "cm_version")
 
@@ -45,7 +48,8 @@ class cm_tiles(ctypes.Structure):
 
 class cm_metadata(ctypes.Structure):
     _fields_ = [("scalars", ctypes.c_void_p), ("seg_bounds", ctypes.c_void_p), ("n_seg", ctypes.c_void_p),
-                ("refs", ctypes.c_void_p), ("n_scalars", ctypes.c_int32), ("n_refs", ctypes.c_int32)]
+                ("refs", ctypes.c_void_p), ("n_scalars", ctypes.c_int32), ("n_refs", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p)]
 
 
 class cm_attn_args(ctypes.Structure):
@@ -79,6 +83,8 @@ def library() -> ctypes.CDLL:
                                     P(ctypes.c_uint32)]),
         "cm_desc_size": (I32, [VP, I32, I32, I32, P(cm_tiles), P(SZ)]),
         "cm_desc_init": (I32, [VP, I32, I32, I32, P(cm_tiles), VP, SZ, P(VP)]),
+        "cm_desc_size_packed": (I32, [VP, I32, I32, I32, P(cm_tiles), P(SZ)]),
+        "cm_desc_init_packed": (I32, [VP, I32, I32, I32, P(cm_tiles), VP, SZ, P(VP)]),
         "cm_desc_free": (None, [VP]),
         "cm_desc_offsets": (I32, [VP, P(SZ)]),
         "cm_build_descriptor": (I32, [VP, P(cm_metadata), VP, VP]),
@@ -191,24 +197,45 @@ def cm_desc_size(spec: Spec, B: int, N: int, seg_cap: int, tiles) -> int:
     return out.value
 
 
-class Descriptor:
-    """A cm_desc handle over a torch uint8 device buffer it keeps alive."""
+def cm_desc_size_packed(spec: Spec, n_samples: int, T: int, seg_cap: int, tiles) -> int:
+    out = ctypes.c_size_t()
+    _check(library().cm_desc_size_packed(spec.handle, n_samples, T, seg_cap, ctypes.byref(make_tiles(tiles)),
+                                         ctypes.byref(out)), "cm_desc_size_packed")
+    return out.value
 
-    def __init__(self, spec: Spec, B: int, N: int, seg_cap: int, tiles, device=None, buffer=None):
+
+class Descriptor:
+    """A cm_desc handle over a torch uint8 device buffer it keeps alive.
+
+    With packed=n_samples (> 0) the descriptor covers one packed sequence of N
+    tokens holding n_samples samples (cm_desc_init_packed); B must then be 1."""
+
+    def __init__(self, spec: Spec, B: int, N: int, seg_cap: int, tiles, device=None, buffer=None, packed: int = 0):
         import torch
 
         self.spec = spec
-        self.B, self.N, self.seg_cap = B, N, seg_cap
+        self.B, self.N, self.seg_cap, self.packed = B, N, seg_cap, int(packed)
+        if self.packed and B != 1:
+            raise ValueError("a packed descriptor covers one sequence: B must be 1")
         self.tiles = tuple(int(x) for x in (tiles if not isinstance(tiles, cm_tiles) else
                                             (tiles.fwd_q, tiles.fwd_k, tiles.bwd_k, tiles.bwd_q)))
-        self.bytes = cm_desc_size(spec, B, N, seg_cap, self.tiles)
+        if self.packed:
+            self.bytes = cm_desc_size_packed(spec, self.packed, N, seg_cap, self.tiles)
+        else:
+            self.bytes = cm_desc_size(spec, B, N, seg_cap, self.tiles)
         if buffer is None:
             buffer = torch.empty(self.bytes, dtype=torch.uint8, device=device or "cuda")
         self.buffer = buffer
         h = ctypes.c_void_p()
-        _check(library().cm_desc_init(spec.handle, B, N, seg_cap, ctypes.byref(make_tiles(self.tiles)),
-                                      ctypes.c_void_p(_ptr(buffer)), buffer.numel() * buffer.element_size(),
-                                      ctypes.byref(h)), "cm_desc_init")
+        if self.packed:
+            _check(library().cm_desc_init_packed(spec.handle, self.packed, N, seg_cap,
+                                                 ctypes.byref(make_tiles(self.tiles)), ctypes.c_void_p(_ptr(buffer)),
+                                                 buffer.numel() * buffer.element_size(), ctypes.byref(h)),
+                   "cm_desc_init_packed")
+        else:
+            _check(library().cm_desc_init(spec.handle, B, N, seg_cap, ctypes.byref(make_tiles(self.tiles)),
+                                          ctypes.c_void_p(_ptr(buffer)), buffer.numel() * buffer.element_size(),
+                                          ctypes.byref(h)), "cm_desc_init")
         self.handle = h.value
         K = cm_spec_info(spec, seg_cap)
         self.K_r, self.K_c = K[0], K[1]
@@ -248,10 +275,12 @@ class DeviceMetadata:
         self.refs = up(md.refs)
         self.n_scalars = int(md.scalars.shape[1])
         self.n_refs = int(md.refs.shape[2]) if md.refs.ndim == 3 else 0
+        cu = getattr(md, "cu_seqlens", None)
+        self.cu_seqlens = None if cu is None else up(cu)
 
     def struct(self) -> cm_metadata:
         return cm_metadata(_ptr(self.scalars), _ptr(self.seg_bounds), _ptr(self.n_seg), _ptr(self.refs),
-                           self.n_scalars, self.n_refs)
+                           self.n_scalars, self.n_refs, _ptr(self.cu_seqlens))
 
 
 def device_metadata(md, device="cuda") -> DeviceMetadata:

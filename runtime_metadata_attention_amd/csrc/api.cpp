@@ -45,7 +45,7 @@ cm_status fill_layout(cm_desc& d) {
     return fail(CM_ERR_INVALID, "more than 4096 tiles along one axis; use larger tiles");
   const size_t B = size_t(d.B), N = size_t(d.N);
   const size_t sizes[8] = {16 * 4,
-                           B * 4,
+                           size_t(d.packed ? d.packed : d.B) * 4,
                            B * d.Tq_f * 4,
                            B * d.Tk_b * 4,
                            B * d.Tq_f * d.Wf * 4,
@@ -61,9 +61,12 @@ cm_status fill_layout(cm_desc& d) {
   return CM_OK;
 }
 
-cm_status make_layout(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap, const cm_tiles* tiles, cm_desc& d) {
+cm_status make_layout(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap, const cm_tiles* tiles, cm_desc& d,
+                      int32_t packed = 0) {
   if (!spec || !tiles) return fail(CM_ERR_NULL, "spec and tiles are required");
   if (B < 1 || N < 1) return fail(CM_ERR_INVALID, "B and N must be >= 1");
+  if (packed < 0 || packed > (1 << 20)) return fail(CM_ERR_INVALID, "n_samples must be in [1, 2^20]");
+  d.packed = packed;
   if (N > (1 << 28)) return fail(CM_ERR_INVALID, "N must be below 2^28");
   if (seg_cap < 0 || seg_cap > 4096) return fail(CM_ERR_INVALID, "seg_cap must be in [0, 4096]");
   if (tiles->fwd_q < 1 || tiles->fwd_k < 1 || tiles->bwd_k < 1 || tiles->bwd_q < 1)
@@ -225,12 +228,12 @@ cm_status cm_desc_size(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_ca
   return CM_OK;
 }
 
-cm_status cm_desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap, const cm_tiles* tiles, void* dev_buf,
-                       size_t bytes, cm_desc** out) {
+static cm_status desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap, const cm_tiles* tiles,
+                           void* dev_buf, size_t bytes, cm_desc** out, int32_t packed) {
   if (!out || !dev_buf) return fail(CM_ERR_NULL, "dev_buf and out are required");
   *out = nullptr;
   cm_desc d;
-  cm_status st = make_layout(spec, B, N, seg_cap, tiles, d);
+  cm_status st = make_layout(spec, B, N, seg_cap, tiles, d, packed);
   if (st != CM_OK) return st;
   if (bytes < d.off[SEC_TOTAL])
     return fail(CM_ERR_SIZE, "descriptor buffer has " + std::to_string(bytes) + " bytes, needs " +
@@ -243,6 +246,28 @@ cm_status cm_desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_ca
   d.bytes = bytes;
   *out = new cm_desc(d);
   return CM_OK;
+}
+
+cm_status cm_desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap, const cm_tiles* tiles, void* dev_buf,
+                       size_t bytes, cm_desc** out) {
+  return desc_init(spec, B, N, seg_cap, tiles, dev_buf, bytes, out, 0);
+}
+
+cm_status cm_desc_size_packed(const cm_spec* spec, int32_t n_samples, int32_t T, int32_t seg_cap, const cm_tiles* tiles,
+                              size_t* bytes) {
+  if (!bytes) return fail(CM_ERR_NULL, "bytes is NULL");
+  if (n_samples < 1) return fail(CM_ERR_INVALID, "n_samples must be >= 1");
+  cm_desc d;
+  cm_status st = make_layout(spec, 1, T, seg_cap, tiles, d, n_samples);
+  if (st != CM_OK) return st;
+  *bytes = d.off[SEC_TOTAL];
+  return CM_OK;
+}
+
+cm_status cm_desc_init_packed(const cm_spec* spec, int32_t n_samples, int32_t T, int32_t seg_cap, const cm_tiles* tiles,
+                              void* dev_buf, size_t bytes, cm_desc** out) {
+  if (n_samples < 1) return fail(CM_ERR_INVALID, "n_samples must be >= 1");
+  return desc_init(spec, 1, T, seg_cap, tiles, dev_buf, bytes, out, n_samples);
 }
 
 void cm_desc_free(cm_desc* desc) { delete desc; }
@@ -264,6 +289,9 @@ cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_des
   if (md->n_scalars > 0 && !md->scalars) return fail(CM_ERR_NULL, "scalars is NULL");
   if (desc->seg_cap > 0 && (!md->seg_bounds || !md->n_seg)) return fail(CM_ERR_NULL, "seg_bounds and n_seg are required");
   if (desc->seg_cap > 0 && md->n_refs > 0 && !md->refs) return fail(CM_ERR_NULL, "refs is NULL");
+  if (desc->packed && !md->cu_seqlens) return fail(CM_ERR_NULL, "a packed descriptor needs md->cu_seqlens");
+  if (!desc->packed && md->cu_seqlens)
+    return fail(CM_ERR_MISMATCH, "md->cu_seqlens is set but the descriptor is not packed (cm_desc_init_packed)");
   const size_t lds = 4 * (size_t(2) * (std::max(desc->Tk_f, desc->Tq_b) + 1) + 2 * 256 + 4 + (desc->seg_cap + 1) +
                           size_t(desc->seg_cap) * md->n_refs + md->n_scalars);
   if (lds > kMaxPreprocessLds) return fail(CM_ERR_INVALID, "metadata too large for the preprocess LDS budget");
@@ -273,6 +301,8 @@ cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_des
   a.seg_bounds = desc->seg_cap > 0 ? md->seg_bounds : nullptr;
   a.n_seg = md->n_seg;
   a.refs = (desc->seg_cap > 0 && md->n_refs > 0) ? md->refs : nullptr;
+  a.cu_seqlens = desc->packed ? md->cu_seqlens : nullptr;
+  a.n_samples = desc->packed;
   a.n_scalars = md->n_scalars;
   a.n_refs = (desc->seg_cap > 0) ? md->n_refs : 0;
   a.seg_cap = desc->seg_cap;

@@ -27,6 +27,7 @@ struct cm_spec {
 struct cm_desc {
   uint64_t spec_id = 0;
   int32_t B = 0, N = 0, seg_cap = 0, K_r = 0, K_c = 0;
+  int32_t packed = 0;            // packed batch: number of samples (B is then 1)
   cm_tiles tiles{};
   int32_t Tq_f = 0, Tk_f = 0, Tk_b = 0, Tq_b = 0, Wf = 0, Wb = 0;
   size_t off[9] = {};            // section offsets + total (same order as cm_desc_offsets)
@@ -52,6 +53,8 @@ struct PreprocessArgs {
   const int32_t* seg_bounds;
   const int32_t* n_seg;
   const int32_t* refs;
+  const int32_t* cu_seqlens;      // packed batch: [n_samples + 1], else NULL
+  int32_t n_samples;              // packed batch: samples (metadata rows), else 0
   int32_t n_scalars, n_refs, seg_cap;
   uint32_t* desc;                 // descriptor base
   int32_t B, N, K_r, K_c;

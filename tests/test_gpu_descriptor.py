@@ -28,11 +28,18 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "descriptor_hashes.js
 
 
 def gpu_descriptor(mask, md, tiles, guard_bytes=0, desc=None, spec=None):
+    """Build the descriptor of `md` (padded or packed) on the GPU; returns its words."""
     spec = spec or cm.cm_spec_compile(specs.BY_MASK[mask])
     if desc is None:
-        size = cm.cm_desc_size(spec, md.B, md.N, md.seg_cap, tiles)
+        if om.is_packed(md):
+            size = cm.cm_desc_size_packed(spec, md.B, md.N, md.seg_cap, tiles)
+        else:
+            size = cm.cm_desc_size(spec, md.B, md.N, md.seg_cap, tiles)
         buf = torch.full((size + guard_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
-        desc = cm.Descriptor(spec, md.B, md.N, md.seg_cap, tiles, buffer=buf)
+        if om.is_packed(md):
+            desc = cm.Descriptor(spec, 1, md.N, md.seg_cap, tiles, buffer=buf, packed=md.B)
+        else:
+            desc = cm.Descriptor(spec, md.B, md.N, md.seg_cap, tiles, buffer=buf)
     dmd = cm.device_metadata(md)
     cm.cm_build_descriptor(spec, dmd, desc)
     torch.cuda.synchronize()
@@ -40,9 +47,9 @@ def gpu_descriptor(mask, md, tiles, guard_bytes=0, desc=None, spec=None):
     return words, desc, spec
 
 
-def explain(words, want, B, N, K_r, K_c, tiles):
-    g = od.View(words, B, N, K_r, K_c, tiles)
-    o = od.View(want, B, N, K_r, K_c, tiles)
+def explain(words, want, B, N, K_r, K_c, tiles, n_err=None):
+    g = od.View(words, B, N, K_r, K_c, tiles, n_err)
+    o = od.View(want, B, N, K_r, K_c, tiles, n_err)
     bad = []
     for name in o.shapes:
         d = np.nonzero(g[name] != o[name])
@@ -64,6 +71,8 @@ def test_full_size_workloads_bit_exact(name):
     got = hashlib.sha256(words.tobytes()).hexdigest()
     if got != gold["sha256"]:
         want = od.build(w.mask, md, desc.K_r, desc.K_c, w.tiles)
+        if om.is_packed(md):
+            pytest.fail(explain(words, want, 1, md.N, desc.K_r, desc.K_c, w.tiles, n_err=md.B))
         pytest.fail(explain(words, want, md.B, md.N, desc.K_r, desc.K_c, w.tiles))
     # nothing written past the end of the descriptor
     tail = desc.buffer[desc.bytes:].cpu().numpy()

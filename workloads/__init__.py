@@ -22,6 +22,11 @@ Readings of underspecified draws (all integer ranges are inclusive):
     until they cover N - g; the last segment is truncated to the remainder.
     Segment 0 references nothing, segment 1 references {0}, segment j >= 2
     references two distinct segments drawn uniformly from {0..j-1}, ascending.
+  * ``hstu_packed_64k`` (stands in for the KuaiRand-1K histories, which are
+    packed variable-length sequences): sample lengths n ~ lognormal(ln 1024,
+    1) floored and clipped to [64, 16384], drawn until they cover 65536 tokens
+    (the last truncated to the remainder); per sample h = max(1, floor(u n)),
+    u ~ U[0.25, 0.94], in the sample's coordinates.
   * Tensors: ``torch.Generator('cpu').manual_seed(seed)``; q, k, v, dO drawn in
     that order with ``randn(B, H, N, d)`` in float32, then rounded to bfloat16.
 """
@@ -40,6 +45,7 @@ __all__ = [
     "make_metadata",
     "make_tensors",
     "metadata_from_segments",
+    "pack_samples",
 ]
 
 
@@ -63,6 +69,11 @@ class Metadata:
     n_seg: np.ndarray
     refs: np.ndarray
     scalar_names: Tuple[str, ...] = ()
+    # packed batches: [B + 1] first token of each sample, cu_seqlens[B] = N
+    # (the B samples are laid end to end as one sequence of N tokens and each
+    # sample's scalars and boundaries are in its own coordinates); None for a
+    # padded batch of B sequences of N tokens
+    cu_seqlens: Optional[np.ndarray] = None
 
     @property
     def seg_cap(self) -> int:
@@ -87,7 +98,8 @@ class Metadata:
 
     def copy(self) -> "Metadata":
         return Metadata(self.B, self.N, self.scalars.copy(), self.seg_bounds.copy(),
-                        self.n_seg.copy(), self.refs.copy(), tuple(self.scalar_names))
+                        self.n_seg.copy(), self.refs.copy(), tuple(self.scalar_names),
+                        None if self.cu_seqlens is None else self.cu_seqlens.copy())
 
 
 @dataclasses.dataclass(frozen=True)
@@ -104,6 +116,7 @@ class Workload:
     n_refs: int
     scalar_names: Tuple[str, ...]
     description: str
+    packed: bool = False   # B = 1 packed sequence of N tokens holding many samples
 
 
 _T128 = (128, 64, 128, 64)
@@ -124,6 +137,10 @@ WORKLOADS: Dict[str, Workload] = {
     "retrieval4_32k": Workload(
         "retrieval4_32k", "retrieval", 1, 16, 32768, 128, 1005, _T128, 64, 2, ("g",),
         "prefix g=512 causal; segment rows see [0,g) u [s_j,i+1) u seg(r1) u seg(r2)"),
+    "hstu_packed_64k": Workload(
+        "hstu_packed_64k", "hstu", 1, 8, 65536, 128, 1006, _T128, 0, 0, ("h",),
+        "packed HSTU batch: heavy-tailed sample lengths n ~ lognormal(ln 1024, 1) clipped to [64, 16384] "
+        "filling 65536 tokens (the last truncated); h = floor(u n), u ~ U[0.25, 0.94]", packed=True),
 }
 
 
@@ -159,6 +176,34 @@ def metadata_from_segments(N: int, seg_cap: int, n_refs: int, scalar_names, per_
             for r, v in enumerate(rl):
                 md.refs[b, j, r] = v
     return md
+
+
+def pack_samples(samples) -> Metadata:
+    """One packed-batch Metadata from one-sample Metadata objects (each with its
+    own length N and the same seg_cap / n_refs / scalar names), laid end to end
+    in the given order."""
+    lens = [int(m.N) for m in samples]
+    cu = np.zeros(len(samples) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    first = samples[0]
+    return Metadata(
+        B=len(samples), N=int(cu[-1]),
+        scalars=np.concatenate([m.scalars[:1] for m in samples]).astype(np.int32),
+        seg_bounds=np.concatenate([m.seg_bounds[:1] for m in samples]).astype(np.int32),
+        n_seg=np.concatenate([m.n_seg[:1] for m in samples]).astype(np.int32),
+        refs=np.concatenate([m.refs[:1] for m in samples]).astype(np.int32),
+        scalar_names=tuple(first.scalar_names),
+        cu_seqlens=cu,
+    )
+
+
+def _draw_packed_lengths(rng: np.random.Generator, T: int):
+    lens = []
+    while sum(lens) < T:
+        n = int(np.clip(np.floor(rng.lognormal(np.log(1024.0), 1.0)), 64, 16384))
+        lens.append(n)
+    lens[-1] = T - sum(lens[:-1])
+    return lens
 
 
 def _draw_shared_prompt(rng: np.random.Generator, N: int, seg_cap: int):
@@ -207,6 +252,13 @@ def make_metadata(w: Workload, seed: Optional[int] = None) -> Metadata:
     if w.name == "shared_prompt_tiny":
         return metadata_from_segments(N, w.seg_cap, w.n_refs, w.scalar_names,
                                       [{"scalars": [64], "bounds": [64, 128, 192, 256]}] * B)
+    if w.packed and w.mask == "hstu":
+        samples = []
+        for n in _draw_packed_lengths(rng, N):
+            m = _empty_md(1, n, w.seg_cap, w.n_refs, w.scalar_names)
+            m.scalars[0, 0] = max(1, int(np.floor(rng.uniform(0.25, 0.94) * n)))
+            samples.append(m)
+        return pack_samples(samples)
     if w.mask == "causal":
         return _empty_md(B, N, w.seg_cap, w.n_refs, w.scalar_names)
     if w.mask == "hstu":
