@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="also time the ordinary-compare masked-interval kernels against the unsigned-check kernels "
                          "on every masked workload (one JSON line per pair to stderr)")
+    ap.add_argument("--predicate", action="store_true",
+                    help="also time the predicate baseline (block mask rebuilt per step, predicate in partial tiles) "
+                         "against the descriptor path on every padded masked workload (JSON lines to stderr)")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the plain copy for counter scaling")
     ap.add_argument("--record-traffic", metavar="DIR", help="write profiles/traffic.json from counter runs in DIR")
     a = ap.parse_args()
@@ -230,11 +233,26 @@ def main():
                    "reduction": round(1.0 - base["ms_per_step"] / abl["ms_per_step"], 4),
                    "unsigned_kernel_ms": base["kernel_ms"], "ordinary_masked_kernel_ms": abl["kernel_ms"]}
             print("[bench-ablation] " + json.dumps(rec), file=sys.stderr, flush=True)
+    if a.predicate:
+        for name in WORKLOADS:
+            if WORKLOADS[name].N < 1024 or WORKLOADS[name].packed:
+                continue
+            base = measure(name, False, a.steps, a.warmup, cpu=False)
+            pred = measure(name, False, a.steps, a.warmup, cpu=False, predicate=True)
+            rec = {"workload": name, "descriptor_ms": base["ms_per_step"], "predicate_ms": pred["ms_per_step"],
+                   "speedup": round(pred["ms_per_step"] / base["ms_per_step"], 4),
+                   "descriptor_build_us": base["preprocess_us"], "blockmask_build_us": pred["preprocess_us"],
+                   "descriptor_kernel_ms": base["kernel_ms"], "predicate_kernel_ms": pred["kernel_ms"]}
+            print("[bench-predicate] " + json.dumps(rec), file=sys.stderr, flush=True)
     line = measure(a.workload, a.causal_path, a.steps, a.warmup, cpu=not a.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 
-def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool, check: int = 0) -> dict:
+def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool, check: int = 0,
+            predicate: bool = False) -> dict:
+    """One bench line.  predicate=True times the predicate baseline: the block
+    mask rebuilt from the metadata every step (cm_build_blockmask) and the
+    predicate evaluated in partial tiles (check CM_CHECK_PREDICATE)."""
     import torch
 
     import runtime_metadata_attention_amd as cm
@@ -252,6 +270,8 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
     spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
     desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev, packed=md.B if w.packed else 0)
     dmd = cm.device_metadata(md, dev)
+    if predicate:
+        check = cm.CM_CHECK_PREDICATE
     args = cm.attn_args(q, causal=causal_path, check=check)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
@@ -266,7 +286,9 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
             if events is not None:
                 events[i].record()
         mark(0)
-        if not causal_path:  # the maskless causal comparator needs no descriptor
+        if predicate:
+            cm.cm_build_blockmask(w.mask, dmd, desc)
+        elif not causal_path:  # the maskless causal comparator needs no descriptor
             cm.cm_build_descriptor(spec, dmd, desc)
         mark(1)
         cm.cm_attn_fwd(args, q, k, v, use_desc, o, lse)
@@ -276,10 +298,11 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
             mark(3 + s)
 
     cm.cm_build_descriptor(spec, dmd, desc)  # (also counts V for the causal comparator)
+    torch.cuda.synchronize()
+    V = visible_pairs(desc, w.H)
     for i in range(warmup):
         step()
     torch.cuda.synchronize()
-    V = visible_pairs(desc, w.H)
     log(f"warmup done; visible pairs V = {V}")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -324,7 +347,7 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tiles": list(w.tiles),
                    "seed": w.seed, "visible_pairs": V, "path": "causal" if causal_path else "descriptor",
                    "packed_samples": int(md.B) if w.packed else 0,
-                   "check": "unsigned" if check == 0 else "ordinary_masked"},
+                   "check": {0: "unsigned", 1: "ordinary_masked", 2: "predicate"}[check]},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "preprocess_us": round(times["preprocess_kernel"] * 1e3, 2),
         "preprocess_GBps": round(pre_bytes / (times["preprocess_kernel"] * 1e-3) / 1e9, 1),

@@ -142,6 +142,9 @@ typedef struct cm_attn_args {
  *     compares and their conjunction per interval.  For measurement only. */
 #define CM_CHECK_UNSIGNED 0
 #define CM_CHECK_ORDINARY_MASKED 1
+/*   CM_CHECK_PREDICATE: the predicate baseline (see cm_build_blockmask); the
+ *     descriptor must come from cm_build_blockmask. */
+#define CM_CHECK_PREDICATE 2
 
 /* ---- offline: MaskSpec -> symbolic endpoints (section 3.2.2) ------------ */
 
@@ -220,6 +223,34 @@ cm_status cm_desc_offsets(const cm_desc* desc, size_t* offsets);
  * set) with the same spec.  Asynchronous on `stream`. */
 cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_desc* desc,
                               cm_stream stream);
+
+/* ---- predicate baseline (for measurement; paper summary, sections 1, 4.2) */
+
+/* The masking the CompileMask pages compare against (FlexAttention style):
+ * the mask as a predicate of (row i, key j), a block mask built per batch by
+ * evaluating it at every element, and the predicate evaluated again at every
+ * element of a partial tile, reading its inputs (each token's segment, a
+ * segment's references) from memory.  Families (CM_PRED_*), as the workloads
+ * define them, with s = metadata scalars[b][0]:
+ *   CM_PRED_CAUSAL         j <= i
+ *   CM_PRED_HSTU           i < s ? j <= i : (j < s || j == i)
+ *   CM_PRED_SHARED_PROMPT  i < s ? j <= i : (j < s || (seg(i) >= 0 && seg(j) == seg(i) && j <= i))
+ *   CM_PRED_RETRIEVAL      i < s ? j <= i : (j < s || seg(i) >= 0 && seg(j) >= 0 &&
+ *                          ((seg(j) == seg(i) && j <= i) || seg(j) is a reference of seg(i)))
+ *                          (at most 2 references per segment)
+ * cm_build_blockmask writes both tile bitmaps, the error words and the
+ * header of a descriptor from cm_desc_init (any spec; padded batches; tiles
+ * of at most 128 rows/keys) and keeps each token's segment in its row_iv
+ * section; the interval tables are not built.  The descriptor then refers to
+ * md's scalars and refs: they must stay unchanged until the attention calls
+ * that use it (with check = CM_CHECK_PREDICATE) have run.  Two launches on
+ * `stream`; the bitmaps equal those cm_build_descriptor makes for the same
+ * mask. */
+#define CM_PRED_CAUSAL 0
+#define CM_PRED_HSTU 1
+#define CM_PRED_SHARED_PROMPT 2
+#define CM_PRED_RETRIEVAL 3
+cm_status cm_build_blockmask(int32_t family, const cm_metadata* md, cm_desc* desc, cm_stream stream);
 
 /* Forward: o (bf16) and lse (fp32, natural log; -inf for a row with no
  * visible key, whose o row is 0).  Requires d in {64, 128} and a descriptor

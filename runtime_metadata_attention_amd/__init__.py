@@ -30,7 +30,7 @@ SECTIONS = ("header", "sample_err", "row_tkmax", "col_tkmax", "fbm", "bbm", "row
 # every symbol include/compilemask.h declares
 EXPORTS = ("cm_spec_compile", "cm_spec_free", "cm_spec_info", "cm_spec_dump", "cm_spec_eval_host",
            "cm_desc_size", "cm_desc_init", "cm_desc_size_packed", "cm_desc_init_packed", "cm_desc_free",
-           "cm_desc_offsets", "cm_build_descriptor",
+           "cm_desc_offsets", "cm_build_descriptor", "cm_build_blockmask",
            "cm_attn_fwd", "cm_attn_bwd_workspace", "cm_attn_bwd", "cm_attn_bwd_stage",
            "cm_status_str", "cm_last_error", "cm_version")
 
@@ -60,6 +60,9 @@ class cm_attn_args(ctypes.Structure):
 
 CM_CHECK_UNSIGNED = 0
 CM_CHECK_ORDINARY_MASKED = 1
+CM_CHECK_PREDICATE = 2
+# predicate-baseline families (cm_build_blockmask)
+CM_PRED = {"causal": 0, "hstu": 1, "shared_prompt": 2, "retrieval": 3}
 
 
 _lib = None
@@ -88,6 +91,7 @@ def library() -> ctypes.CDLL:
         "cm_desc_free": (None, [VP]),
         "cm_desc_offsets": (I32, [VP, P(SZ)]),
         "cm_build_descriptor": (I32, [VP, P(cm_metadata), VP, VP]),
+        "cm_build_blockmask": (I32, [I32, P(cm_metadata), VP, VP]),
         "cm_attn_fwd": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP]),
         "cm_attn_bwd_workspace": (I32, [P(cm_attn_args), P(SZ)]),
         "cm_attn_bwd": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
@@ -285,6 +289,16 @@ class DeviceMetadata:
 
 def device_metadata(md, device="cuda") -> DeviceMetadata:
     return DeviceMetadata(md, device)
+
+
+def cm_build_blockmask(family, md: DeviceMetadata, desc: Descriptor, stream=None):
+    """Predicate baseline: build desc's tile bitmaps by evaluating the family's
+    predicate at every element (family: a CM_PRED name or id).  md must stay
+    alive until the attention calls (check=CM_CHECK_PREDICATE) have run."""
+    fam = CM_PRED[family] if isinstance(family, str) else int(family)
+    m = md.struct()
+    _check(library().cm_build_blockmask(fam, ctypes.byref(m), desc.handle, _stream(stream)), "cm_build_blockmask")
+    desc.pred_md = md  # keep the metadata the descriptor now refers to alive
 
 
 def cm_build_descriptor(spec: Spec, md: DeviceMetadata, desc: Descriptor, stream=None):

@@ -103,6 +103,17 @@ DescView desc_view(const cm_desc* d) {
   v.K_r = d->K_r; v.K_c = d->K_c; v.Wf = d->Wf; v.Wb = d->Wb;
   v.Tq_f = d->Tq_f; v.Tk_f = d->Tk_f; v.Tk_b = d->Tk_b; v.Tq_b = d->Tq_b;
   v.fq = d->tiles.fwd_q; v.fk = d->tiles.fwd_k; v.bk = d->tiles.bwd_k; v.bq = d->tiles.bwd_q;
+  std::memset(&v.pred, 0, sizeof(v.pred));
+  v.pred.family = d->family;
+  if (d->family >= 0) {
+    v.pred.tok_seg = reinterpret_cast<const int32_t*>(base + d->off[SEC_ROW_IV]);
+    v.pred.scalars = d->pred_md.scalars;
+    v.pred.n_scalars = d->pred_md.n_scalars;
+    v.pred.refs = d->seg_cap > 0 ? d->pred_md.refs : nullptr;
+    v.pred.seg_cap = d->seg_cap;
+    v.pred.n_refs = d->seg_cap > 0 ? d->pred_md.n_refs : 0;
+    v.pred.sample_err = reinterpret_cast<const uint32_t*>(base + d->off[SEC_SAMPLE_ERR]);
+  }
   return v;
 }
 
@@ -125,9 +136,11 @@ cm_status check_attn(const cm_attn_args* args, const cm_desc* desc, AttnDims& di
   if (!std::isfinite(args->scale) || args->scale < 0) return fail(CM_ERR_INVALID, "scale must be finite and >= 0");
   dims.scale = args->scale == 0.f ? 1.0f / std::sqrt(float(args->d)) : args->scale;
   dims.causal = args->causal ? 1 : 0;
-  if (args->check != CM_CHECK_UNSIGNED && args->check != CM_CHECK_ORDINARY_MASKED)
-    return fail(CM_ERR_INVALID, "check must be CM_CHECK_UNSIGNED (0) or CM_CHECK_ORDINARY_MASKED (1)");
+  if (args->check != CM_CHECK_UNSIGNED && args->check != CM_CHECK_ORDINARY_MASKED && args->check != CM_CHECK_PREDICATE)
+    return fail(CM_ERR_INVALID, "check must be CM_CHECK_UNSIGNED (0), CM_CHECK_ORDINARY_MASKED (1) or CM_CHECK_PREDICATE (2)");
   dims.check = args->check;
+  if (args->check == CM_CHECK_PREDICATE && dims.causal)
+    return fail(CM_ERR_INVALID, "the predicate baseline runs on a block-mask descriptor, not the maskless causal path");
   std::memset(&view, 0, sizeof(view));
   if (dims.causal) {
     view.fq = 128; view.fk = 64; view.bk = 128; view.bq = 64;
@@ -142,6 +155,9 @@ cm_status check_attn(const cm_attn_args* args, const cm_desc* desc, AttnDims& di
   if (!attn_tiles_supported(args->d, desc->tiles.fwd_q, desc->tiles.fwd_k, desc->tiles.bwd_k, desc->tiles.bwd_q))
     return fail(CM_ERR_UNSUPPORTED, "descriptor tile shape has no attention kernel (supported: forward 64x64 or "
                                     "128x64, backward 64x64 or 128x64)");
+  if ((args->check == CM_CHECK_PREDICATE) != (desc->family >= 0))
+    return fail(CM_ERR_MISMATCH, desc->family >= 0 ? "a block-mask descriptor (cm_build_blockmask) needs check = CM_CHECK_PREDICATE"
+                                                  : "check = CM_CHECK_PREDICATE needs a block-mask descriptor (cm_build_blockmask)");
   view = desc_view(desc);
   return CM_OK;
 }
@@ -278,6 +294,42 @@ cm_status cm_desc_offsets(const cm_desc* desc, size_t* offsets) {
   return CM_OK;
 }
 
+cm_status cm_build_blockmask(int32_t family, const cm_metadata* md, cm_desc* desc, cm_stream stream) {
+  if (!md || !desc) return fail(CM_ERR_NULL, "md and desc are required");
+  if (family < CM_PRED_CAUSAL || family > CM_PRED_RETRIEVAL) return fail(CM_ERR_INVALID, "unknown predicate family");
+  if (desc->packed) return fail(CM_ERR_UNSUPPORTED, "the predicate baseline covers padded batches only");
+  if (md->cu_seqlens) return fail(CM_ERR_MISMATCH, "the predicate baseline covers padded batches only");
+  const int need_scalars = family == CM_PRED_CAUSAL ? 0 : 1;
+  const int need_refs = family == CM_PRED_RETRIEVAL ? 1 : 0;
+  if (md->n_scalars < need_scalars || (need_scalars && !md->scalars))
+    return fail(CM_ERR_MISMATCH, "this family reads one per-sample scalar (metadata scalars[b][0])");
+  if (md->n_refs < 0 || md->n_refs > 2) return fail(CM_ERR_UNSUPPORTED, "the predicate baseline reads at most 2 references per segment");
+  if (need_refs && desc->seg_cap > 0 && md->n_refs > 0 && !md->refs) return fail(CM_ERR_NULL, "refs is NULL");
+  if (desc->seg_cap > 0 && (!md->seg_bounds || !md->n_seg)) return fail(CM_ERR_NULL, "seg_bounds and n_seg are required");
+  if (desc->K_r < 1) return fail(CM_ERR_UNSUPPORTED, "the descriptor's row table is empty (K_row 0): no room for token segments");
+  if (desc->tiles.fwd_q > 128 || desc->tiles.bwd_k > 128)
+    return fail(CM_ERR_UNSUPPORTED, "block masks are built for tiles of at most 128 query rows / keys");
+  PreprocessArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.scalars = md->scalars;
+  a.seg_bounds = desc->seg_cap > 0 ? md->seg_bounds : nullptr;
+  a.n_seg = desc->seg_cap > 0 ? md->n_seg : nullptr;
+  a.refs = (desc->seg_cap > 0 && md->n_refs > 0) ? md->refs : nullptr;
+  a.n_scalars = md->n_scalars;
+  a.n_refs = (desc->seg_cap > 0) ? md->n_refs : 0;
+  a.seg_cap = desc->seg_cap;
+  a.desc = static_cast<uint32_t*>(desc->buf);
+  a.B = desc->B; a.N = desc->N; a.K_r = desc->K_r; a.K_c = desc->K_c;
+  a.fq = desc->tiles.fwd_q; a.fk = desc->tiles.fwd_k; a.bk = desc->tiles.bwd_k; a.bq = desc->tiles.bwd_q;
+  a.Tq_f = desc->Tq_f; a.Tk_f = desc->Tk_f; a.Tk_b = desc->Tk_b; a.Tq_b = desc->Tq_b; a.Wf = desc->Wf; a.Wb = desc->Wb;
+  for (int s = 0; s < 8; ++s) a.off_words[s] = uint32_t(desc->off[s] / 4);
+  hipError_t e = launch_blockmask(a, family, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cm_build_blockmask");
+  desc->family = family;
+  desc->pred_md = *md;
+  return CM_OK;
+}
+
 cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_desc* desc, cm_stream stream) {
   if (!spec || !md || !desc) return fail(CM_ERR_NULL, "spec, md and desc are required");
   if (desc->spec_id != spec->id) return fail(CM_ERR_MISMATCH, "descriptor was initialised for another spec");
@@ -315,6 +367,7 @@ cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_des
   a.dir_off[1] = spec->dir_off[1];
   hipError_t e = launch_preprocess(a, spec->prog, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cm_build_descriptor");
+  desc->family = -1;
   return CM_OK;
 }
 

@@ -60,6 +60,7 @@ struct BwdParams {
   const uint2* col_iv;
   int32_t K_c;
   const uint32_t* col_tkmax;
+  PredCtx pred;            // predicate baseline (check kCheckPredicate) only
 };
 
 constexpr int MAXR = 4;    // column runs held in registers by the dK/dV kernel
@@ -200,8 +201,11 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // this key column's visible query-row runs (in registers when at most MAXR)
-  const int nr = CAUSAL ? 1 : int(uniform(p.col_tkmax[size_t(b) * p.Tk_b + kt]));
-  const uint2* myruns = CAUSAL ? nullptr : p.col_iv + (size_t(b) * N + (kvalid ? key : 0)) * p.K_c;
+  constexpr bool PRED = CHK == kCheckPredicate;
+  const int nr = CAUSAL ? 1 : (PRED ? 0 : int(uniform(p.col_tkmax[size_t(b) * p.Tk_b + kt])));
+  const uint2* myruns = (CAUSAL || PRED) ? nullptr : p.col_iv + (size_t(b) * N + (kvalid ? key : 0)) * p.K_c;
+  PredSample ps;
+  if constexpr (PRED) ps.init(p.pred, b, N);
   const LaneRuns<MAXR> runs =
       load_runs<MAXR>(CAUSAL, make_uint2(uint32_t(key), uint32_t(N)), myruns, nr, kvalid);
 
@@ -305,7 +309,10 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
     // partial and ragged tiles: invisible probabilities are zero
     if ((cs == 2) || ((ct + 1) * BQ > N))
-      mask_tile<CHK>(s, uint32_t(ct * BQ + 4 * h), nr, runs, myruns, kvalid, 0.f);
+    {
+      if constexpr (PRED) mask_pred<false>(s, uint32_t(ct * BQ + 4 * h), key, kvalid, ps, 0.f);
+      else mask_tile<CHK>(s, uint32_t(ct * BQ + 4 * h), nr, runs, myruns, kvalid, 0.f);
+    }
 
     // dS = P (dP - D) of this tile and the bf16 P, dS operands, in eight
     // fenced chunks of four elements, each overlapped with 2NC/8 of the
@@ -427,8 +434,11 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
   const float lse2 = qvalid ? p.lse2[rbase + q] : INFINITY;
   const float Dq = qvalid ? p.D[rbase + q] : 0.f;
 
-  const int nr = CAUSAL ? 1 : int(uniform(p.row_tkmax[size_t(b) * p.Tq_f + qt]));
-  const uint2* myruns = CAUSAL ? nullptr : p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+  constexpr bool PRED = CHK == kCheckPredicate;
+  const int nr = CAUSAL ? 1 : (PRED ? 0 : int(uniform(p.row_tkmax[size_t(b) * p.Tq_f + qt])));
+  const uint2* myruns = (CAUSAL || PRED) ? nullptr : p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+  PredSample ps;
+  if constexpr (PRED) ps.init(p.pred, b, N);
   const LaneRuns<MAXR_Q> runs =
       load_runs<MAXR_Q>(CAUSAL, make_uint2(0u, uint32_t(q + 1)), myruns, nr, qvalid);
 
@@ -516,7 +526,10 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
     }
     // partial and ragged tiles: invisible probabilities are zero
     if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, 0.f);
+    {
+      if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, 0.f);
+      else mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, 0.f);
+    }
 
     // dQ^T += K^T dS^T: dS^T = P^T (dP^T - D) is packed to bf16 one 16-key
     // chunk at a time, fenced so that each chunk's MFMAs overlap the next
@@ -585,6 +598,9 @@ BwdParams make_params(const AttnDims& a, const DescView& dv) {
   p.row_tkmax = dv.row_tkmax;
   p.Wb = dv.Wb; p.bbm = dv.bbm; p.col_iv = reinterpret_cast<const uint2*>(dv.col_iv); p.K_c = dv.K_c;
   p.col_tkmax = dv.col_tkmax;
+  p.pred.family = dv.pred.family; p.pred.tok_seg = dv.pred.tok_seg; p.pred.scalars = dv.pred.scalars;
+  p.pred.n_scalars = dv.pred.n_scalars; p.pred.refs = dv.pred.refs; p.pred.seg_cap = dv.pred.seg_cap;
+  p.pred.n_refs = dv.pred.n_refs; p.pred.sample_err = dv.pred.sample_err;
   return p;
 }
 
@@ -623,10 +639,12 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dvv);
   dim3 grid(p.Tk_b * a.H * a.B);
-  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked;
+  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate;
 #define CM_DKDV(DD, BKK)                                                                                              \
   do {                                                                                                               \
-    if (o) {                                                                                                         \
+    if (pr) {                                                                                                        \
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckPredicate>), grid, dim3(BKK * 2), 0, stream, p);     \
+    } else if (o) {                                                                                                         \
       if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
       else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
     } else {                                                                                                         \
@@ -652,10 +670,12 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
   p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dq = static_cast<uint16_t*>(dq);
   dim3 grid(p.Tq_f * a.H * a.B);
-  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked;
+  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate;
 #define CM_DQ(DD, BMM)                                                                                              \
   do {                                                                                                             \
-    if (o) {                                                                                                       \
+    if (pr) {                                                                                                      \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckPredicate>), grid, dim3(BMM * 2), 0, stream, p);     \
+    } else if (o) {                                                                                                       \
       if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
       else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
     } else {                                                                                                       \

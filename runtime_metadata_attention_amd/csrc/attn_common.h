@@ -310,6 +310,140 @@ __device__ __forceinline__ LaneRuns<MAXR> load_runs(bool causal, uint2 causal_ru
   return lr;
 }
 
+// ------------------------------------------------------------------ predicate baseline
+//
+// The comparison point the CompileMask pages measure against (paper summary,
+// sections 1 and 4.2: FlexAttention-style masking): the mask is a predicate of
+// (row i, key j) evaluated element by element inside partial tiles, with the
+// inputs it needs (the segment of each token, the references of a segment)
+// read from memory at each evaluation.  Families, as the workloads define
+// them:
+//   causal         j <= i
+//   hstu           i < h ? j <= i : (j < h || j == i)
+//   shared_prompt  i < P ? j <= i : (j < P || (seg(i) >= 0 && seg(j) == seg(i) && j <= i))
+//   retrieval      i < g ? j <= i : (j < g || (seg(i) >= 0 && seg(j) >= 0 &&
+//                  ((seg(j) == seg(i) && j <= i) || seg(j) == ref_r(seg(i)) for some r)))
+// (at most two references per segment).
+constexpr int kCheckPredicate = 2;
+enum PredFamily : int { kPredCausal = 0, kPredHstu = 1, kPredSharedPrompt = 2, kPredRetrieval = 3 };
+
+struct PredCtx {
+  int32_t family;
+  const int32_t* tok_seg;    // [B][N] segment of each token, -1 = none
+  const int32_t* scalars;    // [B][n_scalars]; the family's scalar is entry 0
+  int32_t n_scalars;
+  const int32_t* refs;       // [B][seg_cap][n_refs]
+  int32_t seg_cap, n_refs;
+  const uint32_t* sample_err;  // [B], from the block-mask build
+};
+
+// One sample's view of the predicate inputs.
+struct PredSample {
+  int32_t family, N, scalar, n_refs;
+  bool valid;
+  const int32_t* seg;   // [N]
+  const int32_t* refs;  // [seg_cap][n_refs]
+  __device__ __forceinline__ void init(const PredCtx& c, int b, int N_) {
+    family = c.family;
+    N = N_;
+    n_refs = c.n_refs;
+    valid = c.sample_err[b] == 0u;
+    scalar = (c.n_scalars > 0) ? c.scalars[size_t(b) * c.n_scalars] : 0;
+    seg = c.tok_seg + size_t(b) * N_;
+    refs = c.refs ? c.refs + size_t(b) * c.seg_cap * c.n_refs : nullptr;
+  }
+};
+
+// Visibility of (i, j), both inside [0, N); seg_i / seg_j are seg(i) / seg(j)
+// when the caller has them (-2 = read from memory here).
+__device__ __forceinline__ bool pred_visible(const PredSample& p, int i, int j, int seg_i, int seg_j = -2) {
+  if (!p.valid) return false;
+  switch (p.family) {
+    case kPredCausal:
+      return j <= i;
+    case kPredHstu:
+      return i < p.scalar ? j <= i : (j < p.scalar || j == i);
+    case kPredSharedPrompt: {
+      if (i < p.scalar) return j <= i;
+      if (j < p.scalar) return true;
+      const int si = seg_i == -2 ? p.seg[i] : seg_i;
+      return si >= 0 && j <= i && (seg_j == -2 ? p.seg[j] : seg_j) == si;
+    }
+    default: {  // kPredRetrieval
+      if (i < p.scalar) return j <= i;
+      if (j < p.scalar) return true;
+      const int si = seg_i == -2 ? p.seg[i] : seg_i;
+      if (si < 0) return false;
+      const int sj = seg_j == -2 ? p.seg[j] : seg_j;
+      if (sj < 0) return false;
+      if (sj == si) return j <= i;
+      for (int r = 0; r < p.n_refs; ++r)
+        if (p.refs[si * p.n_refs + r] == sj) return true;
+      return false;
+    }
+  }
+}
+
+// The predicate from inputs already in registers: si, sj = seg(i), seg(j);
+// r0, r1 = the references of seg(i) (-1 = none; at most two).
+__device__ __forceinline__ bool pred_eval(int family, bool valid, int scalar, int i, int j, int si, int sj, int r0,
+                                          int r1) {
+  const bool causal = j <= i;
+  bool vis;
+  if (family == kPredCausal) {
+    vis = causal;
+  } else if (family == kPredHstu) {
+    vis = i < scalar ? causal : (j < scalar || j == i);
+  } else if (family == kPredSharedPrompt) {
+    vis = i < scalar ? causal : (j < scalar || (si >= 0 && sj == si && causal));
+  } else {
+    const bool seg_ok = si >= 0 && sj >= 0;
+    vis = i < scalar ? causal : (j < scalar || (seg_ok && ((sj == si && causal) || sj == r0 || sj == r1)));
+  }
+  return valid && vis;
+}
+
+// Partial-tile check of the predicate baseline.  LANE_IS_ROW: the lane owns
+// row `lane_idx` and the tile's elements are keys (forward, dQ); otherwise the
+// lane owns key `lane_idx` and the elements are rows (dK/dV).  The per-token
+// inputs of the tile's elements are gathered first (independent loads, as a
+// tiled predicate kernel loads them for its block), then the predicate is
+// evaluated from registers.  Elements past N are invisible.
+template <bool LANE_IS_ROW>
+__device__ __forceinline__ void mask_pred(f32x16 (&s)[2], uint32_t base, int lane_idx, bool lane_valid,
+                                          const PredSample& ps, float fill) {
+  const bool segs = ps.family >= kPredSharedPrompt;
+  const bool refs = ps.family == kPredRetrieval && ps.n_refs > 0;
+  const int seg_lane = (lane_valid && segs) ? ps.seg[lane_idx] : -1;
+  int lane_r0 = -1, lane_r1 = -1;
+  if (LANE_IS_ROW && refs && seg_lane >= 0) {
+    lane_r0 = ps.refs[seg_lane * ps.n_refs];
+    if (ps.n_refs > 1) lane_r1 = ps.refs[seg_lane * ps.n_refs + 1];
+  }
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {  // one 32-block (16 elements) at a time
+    int se[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int x = int(base + elem_offset(blk, v));
+      se[v] = (segs && x < ps.N) ? ps.seg[x] : -1;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int x = int(base + elem_offset(blk, v));
+      int r0 = lane_r0, r1 = lane_r1;
+      if (!LANE_IS_ROW && refs) {  // the row is the element: its segment's references
+        r0 = se[v] >= 0 ? ps.refs[se[v] * ps.n_refs] : -1;
+        r1 = (se[v] >= 0 && ps.n_refs > 1) ? ps.refs[se[v] * ps.n_refs + 1] : -1;
+      }
+      const int i = LANE_IS_ROW ? lane_idx : x, j = LANE_IS_ROW ? x : lane_idx;
+      const int si = LANE_IS_ROW ? seg_lane : se[v], sj = LANE_IS_ROW ? se[v] : seg_lane;
+      const bool vis = lane_valid && x < ps.N && pred_eval(ps.family, ps.valid, ps.scalar, i, j, si, sj, r0, r1);
+      s[blk][v] = vis ? s[blk][v] : fill;
+    }
+  }
+}
+
 // XCD-aware work-group order.  MI355X deals consecutive work-group ids
 // round-robin to its 8 XCDs, each with its own L2.  With a 1-D grid of
 // tiles * hb work-groups (hb = samples x heads), ids are remapped so that

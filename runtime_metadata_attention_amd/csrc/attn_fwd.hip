@@ -40,6 +40,7 @@ struct FwdParams {
   const uint2* row_iv;
   int32_t K_r;
   const uint32_t* row_tkmax;
+  PredCtx pred;            // predicate baseline (check kCheckPredicate) only
 };
 
 constexpr int BN = 64;
@@ -80,8 +81,11 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   }
 
   // this row's visible runs (in registers when there are at most MAXR)
-  const int nr = CAUSAL ? 1 : int(uniform(p.row_tkmax[size_t(b) * p.Tq + qt]));
-  const uint2* myruns = CAUSAL ? nullptr : p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+  constexpr bool PRED = CHK == kCheckPredicate;
+  const int nr = CAUSAL ? 1 : (PRED ? 0 : int(uniform(p.row_tkmax[size_t(b) * p.Tq + qt])));
+  const uint2* myruns = (CAUSAL || PRED) ? nullptr : p.row_iv + (size_t(b) * N + (qvalid ? q : 0)) * p.K_r;
+  PredSample ps;
+  if constexpr (PRED) ps.init(p.pred, b, N);
   const LaneRuns<MAXR> runs = load_runs<MAXR>(CAUSAL, make_uint2(0u, uint32_t(q + 1)), myruns, nr, qvalid);
 
   f32x16 acc[D / 32];
@@ -130,7 +134,10 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
     // partial tiles (and a ragged last tile): unsigned endpoint checks
     if ((cs == 2) || ((ct + 1) * BN > N))
-      mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, -INFINITY);
+    {
+      if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, -INFINITY);
+      else mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, -INFINITY);
+    }
 
     // online softmax in the log2 domain, scale folded into the exponent.  The
     // running max is only moved (and O rescaled) when some row's max grew by
@@ -209,6 +216,7 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 
 template <int D, int BM>
 hipError_t launch_dc(const FwdParams& p, bool causal, int check, hipStream_t stream) {
+  if (check == kCheckPredicate) return launch<D, BM, false, kCheckPredicate>(p, stream);
   if (check == kCheckOrdinaryMasked)
     return causal ? launch<D, BM, true, kCheckOrdinaryMasked>(p, stream) : launch<D, BM, false, kCheckOrdinaryMasked>(p, stream);
   return causal ? launch<D, BM, true, kCheckUnsigned>(p, stream) : launch<D, BM, false, kCheckUnsigned>(p, stream);
@@ -236,6 +244,9 @@ hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, cons
   p.scale_log2 = a.scale * attn::kLog2e;
   p.fbm = dv.fbm; p.Wf = dv.Wf; p.row_iv = reinterpret_cast<const uint2*>(dv.row_iv); p.K_r = dv.K_r;
   p.row_tkmax = dv.row_tkmax;
+  p.pred.family = dv.pred.family; p.pred.tok_seg = dv.pred.tok_seg; p.pred.scalars = dv.pred.scalars;
+  p.pred.n_scalars = dv.pred.n_scalars; p.pred.refs = dv.pred.refs; p.pred.seg_cap = dv.pred.seg_cap;
+  p.pred.n_refs = dv.pred.n_refs; p.pred.sample_err = dv.pred.sample_err;
   const bool c = a.causal != 0;
   if (a.d == 128) return dv.fq == 128 ? launch_dc<128, 128>(p, c, a.check, stream) : launch_dc<128, 64>(p, c, a.check, stream);
   return dv.fq == 128 ? launch_dc<64, 128>(p, c, a.check, stream) : launch_dc<64, 64>(p, c, a.check, stream);

@@ -28,6 +28,8 @@ struct cm_desc {
   uint64_t spec_id = 0;
   int32_t B = 0, N = 0, seg_cap = 0, K_r = 0, K_c = 0;
   int32_t packed = 0;            // packed batch: number of samples (B is then 1)
+  int32_t family = -1;           // block-mask descriptor of the predicate baseline: its family
+  cm_metadata pred_md{};         // ... and the caller's metadata it refers to
   cm_tiles tiles{};
   int32_t Tq_f = 0, Tk_f = 0, Tk_b = 0, Tq_b = 0, Wf = 0, Wb = 0;
   size_t off[9] = {};            // section offsets + total (same order as cm_desc_offsets)
@@ -64,13 +66,26 @@ struct PreprocessArgs {
   int32_t dir_off[2];
 };
 hipError_t launch_preprocess(const PreprocessArgs& a, const Program& prog, hipStream_t stream);
+// Predicate baseline: per-token segment ids, then both tile bitmaps by
+// evaluating the family's predicate at every element.
+hipError_t launch_blockmask(const PreprocessArgs& a, int family, hipStream_t stream);
 
 struct AttnDims {
   int32_t B, H, N, d;
   int64_t sb, sh, sn;            // element strides of the bf16 tensors
   float scale;
   int32_t causal;
-  int32_t check;                 // partial-tile check: 0 unsigned visible runs, 1 ordinary masked intervals
+  int32_t check;                 // partial-tile check: 0 unsigned visible runs, 1 ordinary masked
+                                 // intervals, 2 the predicate baseline
+};
+struct PredView {                // predicate-baseline inputs (block-mask descriptors)
+  int32_t family;                 // -1: an interval descriptor
+  const int32_t* tok_seg;
+  const int32_t* scalars;
+  int32_t n_scalars;
+  const int32_t* refs;
+  int32_t seg_cap, n_refs;
+  const uint32_t* sample_err;
 };
 struct DescView {                // device pointers into a descriptor
   const uint32_t* fbm;
@@ -81,6 +96,7 @@ struct DescView {                // device pointers into a descriptor
   const uint32_t* col_tkmax;
   int32_t K_r, K_c, Wf, Wb, Tq_f, Tk_f, Tk_b, Tq_b;
   int32_t fq, fk, bk, bq;
+  PredView pred;
 };
 hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, const void* v, const DescView& dv,
                            void* o, float* lse, hipStream_t stream);
