@@ -198,6 +198,9 @@ def main():
     ap.add_argument("--predicate", action="store_true",
                     help="also time the predicate baseline (block mask rebuilt per step, predicate in partial tiles) "
                          "against the descriptor path on every padded masked workload (JSON lines to stderr)")
+    ap.add_argument("--specialize", action="store_true",
+                    help="also time the preprocess of every workload with the interpreting kernel and with the "
+                         "spec-specialised one (cm_spec_specialize); JSON lines to stderr")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the plain copy for counter scaling")
     ap.add_argument("--record-traffic", metavar="DIR", help="write profiles/traffic.json from counter runs in DIR")
     a = ap.parse_args()
@@ -233,6 +236,9 @@ def main():
                    "reduction": round(1.0 - base["ms_per_step"] / abl["ms_per_step"], 4),
                    "unsigned_kernel_ms": base["kernel_ms"], "ordinary_masked_kernel_ms": abl["kernel_ms"]}
             print("[bench-ablation] " + json.dumps(rec), file=sys.stderr, flush=True)
+    if a.specialize:
+        for name in WORKLOADS:
+            print("[bench-specialize] " + json.dumps(time_preprocess(name, a.steps)), file=sys.stderr, flush=True)
     if a.predicate:
         for name in WORKLOADS:
             if WORKLOADS[name].N < 1024 or WORKLOADS[name].packed:
@@ -246,6 +252,41 @@ def main():
             print("[bench-predicate] " + json.dumps(rec), file=sys.stderr, flush=True)
     line = measure(a.workload, a.causal_path, a.steps, a.warmup, cpu=not a.no_cpu_baseline)
     print(json.dumps(line), flush=True)
+
+
+def time_preprocess(name: str, steps: int) -> dict:
+    """Preprocess (metadata -> descriptor) alone, interpreting kernel vs the
+    spec-specialised kernel, on the same buffers; microseconds per build."""
+    import torch
+
+    import runtime_metadata_attention_amd as cm
+    from runtime_metadata_attention_amd import specs
+    from workloads import WORKLOADS, make_metadata
+
+    w = WORKLOADS[name]
+    md = make_metadata(w)
+    dev = torch.device("cuda", 0)
+    dmd = cm.device_metadata(md, dev)
+    out = {"workload": name}
+    t0 = time.perf_counter()
+    for kind in ("interpreted", "specialised"):
+        spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
+        if kind == "specialised":
+            t0 = time.perf_counter()
+            cm.cm_spec_specialize(spec)
+            out["specialise_s"] = round(time.perf_counter() - t0, 3)
+        desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev, packed=md.B if w.packed else 0)
+        for _ in range(3):
+            cm.cm_build_descriptor(spec, dmd, desc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(steps, 10)
+        e0.record()
+        for _ in range(n):
+            cm.cm_build_descriptor(spec, dmd, desc)
+        e1.record()
+        torch.cuda.synchronize()
+        out[kind + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+    return out
 
 
 def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool, check: int = 0,

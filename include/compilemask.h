@@ -214,6 +214,20 @@ cm_status cm_desc_init_packed(const cm_spec* spec, int32_t n_samples, int32_t T,
  * total size.  offsets must hold 9 entries. */
 cm_status cm_desc_offsets(const cm_desc* desc, size_t* offsets);
 
+/* Spec-specialised preprocess (paper summary, sections 1 and 3.1: the spec
+ * is compiled once, every batch reuses the result).  cm_spec_specialize
+ * generates a preprocess kernel in which this spec's lowered program is a
+ * compile-time constant, compiles it with hipRTC for gfx950 (about a second)
+ * and loads it on the current device; from then on cm_build_descriptor with
+ * this spec on that device launches it instead of the interpreting kernel.
+ * The descriptor is bit-identical.  Synchronous, host side; call once per
+ * spec and device.  The modules are unloaded by cm_spec_free.  CM_ERR_HIP
+ * (with the compiler log in cm_last_error) if hipRTC or the loader fails.
+ * cm_spec_codegen returns the generated source (same conventions as
+ * cm_spec_dump). */
+cm_status cm_spec_specialize(cm_spec* spec);
+cm_status cm_spec_codegen(const cm_spec* spec, char* buf, size_t len, size_t* needed);
+
 /* ---- online, every batch (section 3.3) --------------------------------- */
 
 /* One preprocess kernel launch: evaluate the compiled endpoints of `spec`

@@ -29,6 +29,7 @@ STATUS = {0: "CM_OK", -1: "CM_ERR_NULL", -2: "CM_ERR_INVALID", -3: "CM_ERR_PARSE
 SECTIONS = ("header", "sample_err", "row_tkmax", "col_tkmax", "fbm", "bbm", "row_iv", "col_iv", "total")
 # every symbol include/compilemask.h declares
 EXPORTS = ("cm_spec_compile", "cm_spec_free", "cm_spec_info", "cm_spec_dump", "cm_spec_eval_host",
+           "cm_spec_specialize", "cm_spec_codegen",
            "cm_desc_size", "cm_desc_init", "cm_desc_size_packed", "cm_desc_init_packed", "cm_desc_free",
            "cm_desc_offsets", "cm_build_descriptor", "cm_build_blockmask",
            "cm_attn_fwd", "cm_attn_bwd_workspace", "cm_attn_bwd", "cm_attn_bwd_stage",
@@ -82,6 +83,8 @@ def library() -> ctypes.CDLL:
         "cm_spec_free": (None, [VP]),
         "cm_spec_info": (I32, [VP, I32, P(I32), P(I32), P(I32), P(I32)]),
         "cm_spec_dump": (I32, [VP, ctypes.c_char_p, SZ, P(SZ)]),
+        "cm_spec_specialize": (I32, [VP]),
+        "cm_spec_codegen": (I32, [VP, ctypes.c_char_p, SZ, P(SZ)]),
         "cm_spec_eval_host": (I32, [VP, I32, I32, I32, VP, I32, VP, I32, I32, VP, I32, VP, I32, P(I32),
                                     P(ctypes.c_uint32)]),
         "cm_desc_size": (I32, [VP, I32, I32, I32, P(cm_tiles), P(SZ)]),
@@ -161,6 +164,21 @@ def cm_spec_dump(spec: Spec) -> str:
     buf = ctypes.create_string_buffer(need.value)
     _check(library().cm_spec_dump(spec.handle, buf, need.value, None), "cm_spec_dump")
     return buf.value.decode()
+
+
+def cm_spec_codegen(spec: Spec) -> str:
+    """HIP source of the spec-specialised preprocess kernel."""
+    need = ctypes.c_size_t()
+    _check(library().cm_spec_codegen(spec.handle, None, 0, ctypes.byref(need)), "cm_spec_codegen")
+    buf = ctypes.create_string_buffer(need.value)
+    _check(library().cm_spec_codegen(spec.handle, buf, need.value, None), "cm_spec_codegen")
+    return buf.value.decode()
+
+
+def cm_spec_specialize(spec: Spec):
+    """Compile (hipRTC) and load the spec-specialised preprocess kernel on the
+    current device; later cm_build_descriptor calls with this spec use it."""
+    _check(library().cm_spec_specialize(spec.handle), "cm_spec_specialize")
 
 
 def cm_spec_eval_host(spec: Spec, direction: int, N: int, index: int, scalars: Sequence[int],

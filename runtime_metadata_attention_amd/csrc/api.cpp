@@ -365,7 +365,9 @@ cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_des
   for (int s = 0; s < 8; ++s) a.off_words[s] = uint32_t(desc->off[s] / 4);
   a.dir_off[0] = spec->dir_off[0];
   a.dir_off[1] = spec->dir_off[1];
-  hipError_t e = launch_preprocess(a, spec->prog, static_cast<hipStream_t>(stream));
+  void* fn = specialized_function(spec);
+  hipError_t e = fn ? launch_specialized(fn, a, static_cast<hipStream_t>(stream))
+                    : launch_preprocess(a, spec->prog, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cm_build_descriptor");
   desc->family = -1;
   return CM_OK;

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "compilemask.h"
+#include "preprocess_args.h"
 #include "program.h"
 
 struct cm_spec {
@@ -22,6 +23,14 @@ struct cm_spec {
   int n_refs = 0;
   uint64_t id = 0;               // unique per compiled spec
   std::string listing;           // human-readable lowered program
+  // spec-specialised preprocess kernels (cm_spec_specialize), one per device
+  struct Specialized {
+    int device;
+    void* module;                // hipModule_t
+    void* function;              // hipFunction_t
+  };
+  std::vector<Specialized> specialized;
+  ~cm_spec();
 };
 
 struct cm_desc {
@@ -39,8 +48,6 @@ struct cm_desc {
 
 namespace cm {
 
-enum Section { SEC_HEADER = 0, SEC_SAMPLE_ERR, SEC_ROW_TKMAX, SEC_COL_TKMAX, SEC_FBM, SEC_BBM,
-               SEC_ROW_IV, SEC_COL_IV, SEC_TOTAL };
 
 // Thread-local error detail for cm_last_error().
 void set_error(const std::string& msg);
@@ -50,22 +57,13 @@ cm_status fail(cm_status st, const std::string& msg);
 int spec_width(const cm_spec* spec, int dir, int seg_cap);
 
 // Kernel launchers (HIP translation units).
-struct PreprocessArgs {
-  const int32_t* scalars;
-  const int32_t* seg_bounds;
-  const int32_t* n_seg;
-  const int32_t* refs;
-  const int32_t* cu_seqlens;      // packed batch: [n_samples + 1], else NULL
-  int32_t n_samples;              // packed batch: samples (metadata rows), else 0
-  int32_t n_scalars, n_refs, seg_cap;
-  uint32_t* desc;                 // descriptor base
-  int32_t B, N, K_r, K_c;
-  int32_t fq, fk, bk, bq;         // tile sizes
-  int32_t Tq_f, Tk_f, Tk_b, Tq_b, Wf, Wb;
-  uint32_t off_words[8];          // section offsets in words
-  int32_t dir_off[2];
-};
 hipError_t launch_preprocess(const PreprocessArgs& a, const Program& prog, hipStream_t stream);
+size_t preprocess_lds_bytes(const PreprocessArgs& a);
+// The spec-specialised kernel for the current device, or NULL.
+void* specialized_function(const cm_spec* spec);
+hipError_t launch_specialized(void* function, const PreprocessArgs& a, hipStream_t stream);
+// HIP source of the spec-specialised preprocess kernel.
+std::string specialized_source(const cm_spec* spec);
 // Predicate baseline: per-token segment ids, then both tile bitmaps by
 // evaluating the family's predicate at every element.
 hipError_t launch_blockmask(const PreprocessArgs& a, int family, hipStream_t stream);

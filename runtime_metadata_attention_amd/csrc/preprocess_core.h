@@ -1,0 +1,307 @@
+// preprocess_core.h -- the preprocess kernel's device code (batch metadata ->
+// Execution Descriptor), shared by two instantiations:
+//   * preprocess.hip: the lowered program read from the kernel arguments and
+//     interpreted (every spec, no compile step);
+//   * a spec-specialised kernel compiled at run time (cm_spec_specialize):
+//     the same code with the program as a compile-time constant array, which
+//     the compiler folds into straight-line endpoint arithmetic.
+// See preprocess.hip for what the kernel computes.  This header is
+// self-contained (HIP device code, program.h and preprocess_args.h) so that
+// the run-time compiler can take it as is.
+#pragma once
+#include "preprocess_args.h"
+#include "program.h"
+
+namespace cm {
+namespace pre {
+
+constexpr int kThreads = kPreThreads;
+
+struct Role {
+  int x0, nidx;          // first index and index count of this tile
+  int K;                 // table width
+  uint2* table;          // this sample's interval table
+  int Bt, T, W;          // tile width / count / words along the other axis
+  uint32_t* bitmap;      // this tile's bitmap row
+  uint32_t* tkmax;       // this tile's run maximum
+  int dir_off;
+};
+
+struct Lds {
+  int32_t* any;
+  int32_t* full;
+  int32_t* misc;         // [0] run max, [1] sample error, [2] error OR over samples, [3] cu_seqlens error
+};
+
+__device__ __forceinline__ void count_run(const Lds& L, const Role& r, int N, uint32_t s, uint32_t e) {
+  const int a0 = int(s) / r.Bt, a1 = int(e - 1) / r.Bt;
+  atomicAdd(&L.any[a0], 1);
+  atomicAdd(&L.any[a1 + 1], -1);
+  const int f0 = (int(s) + r.Bt - 1) / r.Bt;
+  const int f1 = (int(e) == N) ? r.T : int(e) / r.Bt;
+  if (f0 < f1) {
+    atomicAdd(&L.full[f0], 1);
+    atomicAdd(&L.full[f1], -1);
+  }
+}
+
+// Where an index's rule is evaluated: the sample's metadata, the index in the
+// sample's coordinates, and the shift from those to the descriptor's (0 for a
+// padded batch; the sample's first token for a packed one).
+struct Site {
+  SampleView sv;
+  int local;       // index inside the sample
+  int global;      // index in the descriptor (its table row)
+  uint32_t shift;  // added to the evaluated endpoints
+};
+
+// Runs held in registers: sorted insertion with compile-time indices only.
+template <int KC>
+__device__ __forceinline__ void runs_registers(const int32_t* prog, const Site& st, const Role& r, const Lds& L, int N) {
+  uint32_t s[KC], e[KC];
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < KC; ++q) { s[q] = 0; e[q] = 0; }
+  eval_direction(prog, r.dir_off, st.sv, st.local, [&](int32_t lo_, int32_t hi_) {
+    const uint32_t lo = uint32_t(lo_) + st.shift, hi = uint32_t(hi_) + st.shift;
+    int pos = 0;
+#pragma unroll
+    for (int q = 0; q < KC; ++q) pos += (q < n && s[q] <= lo) ? 1 : 0;
+#pragma unroll
+    for (int q = KC - 1; q >= 0; --q) {
+      if (q > 0 && q > pos && q <= n) { s[q] = s[q - 1]; e[q] = e[q - 1]; }
+      else if (q == pos) { s[q] = lo; e[q] = hi; }
+    }
+    n = n < KC ? n + 1 : KC;
+  });
+  uint2* row = r.table + size_t(st.global) * r.K;
+  int nout = 0;
+  uint32_t cs = 0, ce = 0;
+  bool open = false;
+#pragma unroll
+  for (int q = 0; q < KC; ++q) {
+    if (q < n) {
+      if (open && s[q] <= ce) {
+        ce = e[q] > ce ? e[q] : ce;
+      } else {
+        if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, N, cs, ce); }
+        cs = s[q]; ce = e[q]; open = true;
+      }
+    }
+  }
+  if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, N, cs, ce); }
+  for (int q = nout; q < r.K; ++q) row[q] = make_uint2(0u, 0u);
+  atomicMax(&L.misc[0], nout);
+}
+
+// Wide tables (exists-slots): sort and merge in the index's own table row.
+__device__ __forceinline__ void runs_memory(const int32_t* prog, const Site& st, const Role& r, const Lds& L, int N) {
+  uint2* row = r.table + size_t(st.global) * r.K;
+  int n = 0;
+  const int K = r.K;
+  eval_direction(prog, r.dir_off, st.sv, st.local, [&](int32_t lo_, int32_t hi_) {
+    if (n >= K) return;
+    const uint32_t lo = uint32_t(lo_) + st.shift, hi = uint32_t(hi_) + st.shift;
+    int pos = n;
+    while (pos > 0 && row[pos - 1].x > lo) { row[pos] = row[pos - 1]; --pos; }
+    row[pos] = make_uint2(lo, hi);
+    ++n;
+  });
+  int nout = 0;
+  uint32_t cs = 0, ce = 0;
+  bool open = false;
+  for (int q = 0; q < n; ++q) {
+    const uint2 v = row[q];
+    if (open && v.x <= ce) {
+      ce = v.y > ce ? v.y : ce;
+    } else {
+      if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, N, cs, ce); }
+      cs = v.x; ce = v.y; open = true;
+    }
+  }
+  if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, N, cs, ce); }
+  for (int q = nout; q < K; ++q) row[q] = make_uint2(0u, 0u);
+  atomicMax(&L.misc[0], nout);
+}
+
+// In-place inclusive prefix sums of a[0..T) and b[0..T) by one work-group.
+__device__ void scan2(int32_t* a, int32_t* b, int T, int32_t* part) {
+  const int t = threadIdx.x;
+  const int chunk = (T + kThreads - 1) / kThreads;
+  const int lo = t * chunk, hi = min(T, lo + chunk);
+  int32_t sa = 0, sb = 0;
+  for (int c = lo; c < hi; ++c) { sa += a[c]; sb += b[c]; }
+  part[t] = sa;
+  part[kThreads + t] = sb;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    int32_t va = 0, vb = 0;
+    if (t >= off) { va = part[t - off]; vb = part[kThreads + t - off]; }
+    __syncthreads();
+    part[t] += va;
+    part[kThreads + t] += vb;
+    __syncthreads();
+  }
+  int32_t ra = t > 0 ? part[t - 1] : 0, rb = t > 0 ? part[kThreads + t - 1] : 0;
+  for (int c = lo; c < hi; ++c) {
+    ra += a[c]; a[c] = ra;
+    rb += b[c]; b[c] = rb;
+  }
+  __syncthreads();
+}
+
+// The kernel body for one work-group; `prog` is the lowered program (both
+// directions).  Grid (Tq_f + Tk_b, B), kThreads threads, dynamic LDS of
+// preprocess_lds_words(a) words.
+__device__ __forceinline__ void preprocess_body(const PreprocessArgs& a, const int32_t* prog) {
+  extern __shared__ int32_t lds[];
+  const int b = blockIdx.y;
+  const bool row_role = int(blockIdx.x) < a.Tq_f;
+  const int tile = row_role ? int(blockIdx.x) : int(blockIdx.x) - a.Tq_f;
+  uint32_t* desc = a.desc;
+
+  Role r;
+  if (row_role) {
+    r.x0 = tile * a.fq; r.nidx = min(a.fq, a.N - r.x0); r.K = a.K_r;
+    r.table = reinterpret_cast<uint2*>(desc + a.off_words[SEC_ROW_IV]) + size_t(b) * a.N * a.K_r;
+    r.Bt = a.fk; r.T = a.Tk_f; r.W = a.Wf;
+    r.bitmap = desc + a.off_words[SEC_FBM] + (size_t(b) * a.Tq_f + tile) * a.Wf;
+    r.tkmax = desc + a.off_words[SEC_ROW_TKMAX] + size_t(b) * a.Tq_f + tile;
+    r.dir_off = a.dir_off[0];
+  } else {
+    r.x0 = tile * a.bk; r.nidx = min(a.bk, a.N - r.x0); r.K = a.K_c;
+    r.table = reinterpret_cast<uint2*>(desc + a.off_words[SEC_COL_IV]) + size_t(b) * a.N * a.K_c;
+    r.Bt = a.bq; r.T = a.Tq_b; r.W = a.Wb;
+    r.bitmap = desc + a.off_words[SEC_BBM] + (size_t(b) * a.Tk_b + tile) * a.Wb;
+    r.tkmax = desc + a.off_words[SEC_COL_TKMAX] + size_t(b) * a.Tk_b + tile;
+    r.dir_off = a.dir_off[1];
+  }
+
+  // LDS: any[Tmax+1] full[Tmax+1] part[2*threads] misc[4] bounds[seg_cap+1] refs[..] scalars[..]
+  const int Tmax = max(a.Tk_f, a.Tq_b);
+  Lds L;
+  L.any = lds;
+  L.full = lds + (Tmax + 1);
+  int32_t* part = L.full + (Tmax + 1);
+  L.misc = part + 2 * kThreads;
+  int32_t* bounds = L.misc + 4;
+  int32_t* refs = bounds + (a.seg_cap + 1);
+  int32_t* scal = refs + a.seg_cap * a.n_refs;
+
+  const int tid = threadIdx.x;
+  const bool packed = a.cu_seqlens != nullptr;
+  const int n_meta = packed ? a.n_samples : a.B;  // metadata rows
+  // a padded batch caches sample b's metadata in LDS; a packed batch reads
+  // each index's sample from global memory
+  const int n_seg = (!packed && a.n_seg) ? a.n_seg[b] : 0;
+  if (!packed) {
+    for (int t = tid; t <= a.seg_cap && a.seg_bounds; t += kThreads) bounds[t] = a.seg_bounds[size_t(b) * (a.seg_cap + 1) + t];
+    for (int t = tid; t < a.seg_cap * a.n_refs; t += kThreads) refs[t] = a.refs[size_t(b) * a.seg_cap * a.n_refs + t];
+    for (int t = tid; t < a.n_scalars; t += kThreads) scal[t] = a.scalars[size_t(b) * a.n_scalars + t];
+  }
+  for (int t = tid; t <= r.T; t += kThreads) { L.any[t] = 0; L.full[t] = 0; }
+  if (tid == 0) { L.misc[0] = 0; L.misc[1] = 0; L.misc[2] = 0; L.misc[3] = 0; }
+  __syncthreads();
+  if (packed) {
+    // cu_seqlens must run from 0 to N without decreasing
+    for (int t = tid; t <= a.n_samples; t += kThreads) {
+      const int c = a.cu_seqlens[t];
+      const bool bad = (t == 0 && c != 0) || (t == a.n_samples && c != a.N) ||
+                       (t < a.n_samples && a.cu_seqlens[t + 1] < c) || c < 0 || c > a.N;
+      if (bad) atomicOr(reinterpret_cast<uint32_t*>(&L.misc[3]), kMdCuSeqlens);
+    }
+  } else if (tid == 0) {
+    L.misc[1] = int32_t(validate_sample(a.N, n_seg, a.seg_cap, bounds, refs, a.n_refs));
+  }
+  __syncthreads();
+  const uint32_t cu_err = uint32_t(L.misc[3]);
+  // work-group 0 (of sample 0) forms the error word of every sample; a padded
+  // batch's work-groups (0, b) also write sample_err[b] below
+  if (blockIdx.x == 0 && b == 0) {
+    for (int bb = tid; bb < n_meta; bb += kThreads) {
+      const int ns = a.n_seg ? a.n_seg[bb] : 0;
+      const int32_t* gb = a.seg_bounds ? a.seg_bounds + size_t(bb) * (a.seg_cap + 1) : nullptr;
+      const int32_t* gr = a.refs ? a.refs + size_t(bb) * a.seg_cap * a.n_refs : nullptr;
+      uint32_t e;
+      if (packed && cu_err) {
+        e = cu_err;  // no sample boundaries to check against: every row is empty
+      } else {
+        const int nlen = packed ? a.cu_seqlens[bb + 1] - a.cu_seqlens[bb] : a.N;
+        e = validate_sample(nlen, ns, a.seg_cap, gb, gr, a.n_refs);
+      }
+      if (packed) desc[a.off_words[SEC_SAMPLE_ERR] + bb] = e;
+      atomicOr(reinterpret_cast<uint32_t*>(&L.misc[2]), e);
+    }
+  }
+  __syncthreads();
+  const uint32_t err = uint32_t(L.misc[1]);
+
+  for (int q = tid; q < r.nidx; q += kThreads) {
+    const int idx = r.x0 + q;
+    Site st;
+    st.global = idx;
+    bool skip;
+    if (!packed) {
+      st.sv.N = a.N; st.sv.n_seg = n_seg; st.sv.n_refs = a.n_refs;
+      st.sv.scalars = scal; st.sv.bounds = bounds; st.sv.refs = refs;
+      st.local = idx;
+      st.shift = 0;
+      skip = err != 0;
+    } else {
+      skip = cu_err != 0;
+      if (!skip) {
+        // the sample holding idx: the last one whose first token is <= idx
+        int lo = 0, hi = a.n_samples - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (a.cu_seqlens[mid] <= idx) lo = mid; else hi = mid - 1;
+        }
+        const int sb = lo, c0 = a.cu_seqlens[sb];
+        const int ns = a.n_seg ? a.n_seg[sb] : 0;
+        st.sv.N = a.cu_seqlens[sb + 1] - c0;
+        st.sv.n_seg = ns; st.sv.n_refs = a.n_refs;
+        st.sv.scalars = a.scalars ? a.scalars + size_t(sb) * a.n_scalars : nullptr;
+        st.sv.bounds = a.seg_bounds ? a.seg_bounds + size_t(sb) * (a.seg_cap + 1) : nullptr;
+        st.sv.refs = a.refs ? a.refs + size_t(sb) * a.seg_cap * a.n_refs : nullptr;
+        st.local = idx - c0;
+        st.shift = uint32_t(c0);
+        skip = validate_sample(st.sv.N, ns, a.seg_cap, st.sv.bounds, st.sv.refs, a.n_refs) != 0;
+      }
+    }
+    if (skip) {
+      uint2* row = r.table + size_t(idx) * r.K;
+      for (int t = 0; t < r.K; ++t) row[t] = make_uint2(0u, 0u);
+      continue;
+    }
+    if (r.K <= 1) runs_registers<1>(prog, st, r, L, a.N);
+    else if (r.K <= 2) runs_registers<2>(prog, st, r, L, a.N);
+    else if (r.K <= 4) runs_registers<4>(prog, st, r, L, a.N);
+    else if (r.K <= 8) runs_registers<8>(prog, st, r, L, a.N);
+    else runs_memory(prog, st, r, L, a.N);
+  }
+  __syncthreads();
+  scan2(L.any, L.full, r.T, part);
+
+  for (int w = tid; w < r.W; w += kThreads) {
+    uint32_t word = 0;
+    for (int c = 16 * w; c < min(r.T, 16 * w + 16); ++c) {
+      const uint32_t code = L.any[c] == 0 ? 0u : (L.full[c] == r.nidx ? 1u : 2u);
+      word |= code << (2 * (c - 16 * w));
+    }
+    r.bitmap[w] = word;
+  }
+  if (tid == 0) {
+    *r.tkmax = uint32_t(L.misc[0]);
+    if (blockIdx.x == 0 && !packed) desc[a.off_words[SEC_SAMPLE_ERR] + b] = err;
+    if (blockIdx.x == 0 && b == 0) {
+      uint4* h = reinterpret_cast<uint4*>(desc + a.off_words[SEC_HEADER]);
+      h[0] = make_uint4(kDescMagic, uint32_t(a.B), uint32_t(a.N), uint32_t(a.K_r));
+      h[1] = make_uint4(uint32_t(a.K_c), uint32_t(a.fq), uint32_t(a.fk), uint32_t(a.bk));
+      h[2] = make_uint4(uint32_t(a.bq), uint32_t(a.Tq_f), uint32_t(a.Tk_f), uint32_t(a.Tk_b));
+      h[3] = make_uint4(uint32_t(a.Tq_b), uint32_t(L.misc[2]), uint32_t(a.seg_cap), uint32_t(a.n_samples));
+    }
+  }
+}
+
+}  // namespace pre
+}  // namespace cm

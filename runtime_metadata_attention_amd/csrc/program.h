@@ -27,9 +27,19 @@
 // that is absent) is false.  An index uses the first Region whose guard holds;
 // an index in no Region sees nothing.
 #pragma once
+#ifdef __HIPCC_RTC__
+// the run-time compiler keeps the fixed-width types in its own namespace
+typedef __hip_internal::int32_t int32_t;
+typedef __hip_internal::uint32_t uint32_t;
+typedef __hip_internal::int64_t int64_t;
+typedef __hip_internal::uint64_t uint64_t;
+#else
 #include <stdint.h>
+#endif
 
-#if defined(__HIPCC__) || defined(__HIP__)
+#if defined(__HIPCC_RTC__)
+#define CM_HD __host__ __device__ __forceinline__
+#elif defined(__HIPCC__) || defined(__HIP__)
 #include <hip/hip_runtime.h>
 #define CM_HD __host__ __device__ __forceinline__
 #else

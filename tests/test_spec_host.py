@@ -187,3 +187,25 @@ def test_argument_checks_without_gpu():
     st = cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None)
     assert st == -2  # no such partial-tile check
     assert cm.cm_status_str(-4) == "descriptor/spec/argument mismatch"
+
+
+def test_specialised_source_embeds_the_program_and_compiles():
+    """The generated preprocess source holds the lowered program as a constant
+    array and builds for gfx950 against the library's own headers."""
+    import os
+    import subprocess
+    import tempfile
+
+    spec = cm.cm_spec_compile(specs.RETRIEVAL)
+    src = cm.cm_spec_codegen(spec)
+    assert "kProgram[" in src and "preprocess_body(a, kProgram)" in src
+    words = src.split("kProgram[")[1].split("]")[0]
+    assert int(words) > 10
+    csrc = os.path.join(os.path.dirname(cm.__file__), "csrc")
+    with tempfile.TemporaryDirectory() as d:
+        f = os.path.join(d, "spec.hip")
+        open(f, "w").write("#include <hip/hip_runtime.h>\n" + src)
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "-std=c++17", "-O1", "--offload-arch=gfx950", "--cuda-device-only",
+                            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                            "-I", csrc, "-c", f, "-o", os.path.join(d, "spec.o")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
