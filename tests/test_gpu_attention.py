@@ -168,6 +168,19 @@ def test_ordinary_masked_check_equals_unsigned_check_bitwise(mask, N, d, tiles, 
     check_all(b, t, mask, md)
 
 
+def test_columns_with_twenty_runs_parity():
+    """Key columns with 20 visible-row runs: the dK/dV kernel's memory path for
+    runs beyond its register copy, and the preprocess's beyond 16 intervals."""
+    L, S = 40, 40
+    N = 40 + L * S
+    bounds = [40 + L * k for k in range(S + 1)]
+    refs = [[], []] + [[0] if k % 2 == 0 else [1, k - 1] for k in range(2, S)]
+    md = metadata_from_segments(N, S, 2, ("g",), [{"scalars": [40], "bounds": bounds, "refs": refs}])
+    t = make_tensors(1, 2, N, 128, 61)
+    out = run_gpu(specs.RETRIEVAL, md, t, (128, 64, 128, 64))
+    check_all(out, t, "retrieval", md)
+
+
 def test_ordinary_masked_check_on_the_causal_path():
     N = 700
     md = small_md("causal", N=N, B=1)

@@ -101,6 +101,24 @@ def test_small_ragged_cases_bit_exact(mask, N, tiles, seed):
     assert (desc.buffer[desc.bytes:].cpu().numpy() == 0xA5).all()
 
 
+def test_wide_columns_beyond_the_register_runs_use_the_memory_path():
+    """Segment 0 referenced by every even segment (non-adjacent: separate runs)
+    and segment 1 by every odd one: their key columns receive about 20
+    intervals each, more than the preprocess keeps in registers (16)."""
+    L, S = 40, 40
+    N = 40 + L * S
+    bounds = [40 + L * k for k in range(S + 1)]
+    refs = [[], []] + [[0] if k % 2 == 0 else [1, k - 1] for k in range(2, S)]
+    md = metadata_from_segments(N, S, 2, ("g",), [{"scalars": [40], "bounds": bounds, "refs": refs}] * 2)
+    M = om.dense_mask("retrieval", md, 0).astype(np.int8)
+    starts = np.diff(np.vstack([np.zeros((1, N), np.int8), M]), axis=0) == 1
+    assert starts.sum(axis=0).max() > 16
+    tiles = (128, 64, 128, 64)
+    words, desc, _ = gpu_descriptor("retrieval", md, tiles)
+    want = od.build("retrieval", md, desc.K_r, desc.K_c, tiles)
+    assert np.array_equal(words, want), explain(words, want, md.B, N, desc.K_r, desc.K_c, tiles)
+
+
 def test_rebuild_reuses_spec_and_overwrites_everything():
     """Same spec and descriptor, metadata redrawn (HSTU h changes per batch)."""
     tiles = (128, 64, 128, 64)
