@@ -316,11 +316,11 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // dS = P (dP - D) of this tile and the bf16 P, dS operands, in eight
     // fenced chunks of four elements, each overlapped with 2NC/8 of the
-    // previous tile's dV/dK MFMAs (operands read four MFMAs ahead, D one
+    // previous tile's dV/dK MFMAs (operands read two MFMAs ahead, D one
     // chunk ahead).
     bf16x8 pb[4], db8[4];
     {
-      constexpr int NM = 2 * NC, G = 4, MPC = NM / 8;
+      constexpr int NM = 2 * NC, G = 2, MPC = NM / 8;
       const char* prv = lds0 + pbuf * (2 * TB);
       bf16x8 op[NM];
 #pragma unroll
