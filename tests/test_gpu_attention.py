@@ -96,6 +96,35 @@ def test_small_ragged_parity(mask, N, d, tiles, seed):
     check_all(out, t, mask, md)
 
 
+def tiny_sequences():
+    """Sequences shorter than one wave's 32 rows, each sample a degenerate
+    shape of its family: no history (HSTU rows that see only themselves), a
+    prompt that fills the sequence, a segment of one token, a reference to a
+    one-token segment."""
+    seg = metadata_from_segments
+    return [
+        ("causal", seg(1, 0, 0, (), [{}] * 2)),
+        ("causal", seg(5, 0, 0, (), [{}] * 2)),
+        ("hstu", seg(1, 0, 0, ("h",), [{"scalars": [0]}, {"scalars": [1]}])),
+        ("hstu", seg(5, 0, 0, ("h",), [{"scalars": [0]}, {"scalars": [5]}])),
+        ("shared_prompt", seg(1, 2, 0, ("P",), [{"scalars": [1]}, {"scalars": [0], "bounds": [0, 1]}])),
+        ("shared_prompt", seg(5, 2, 0, ("P",), [{"scalars": [2], "bounds": [2, 3, 5]}, {"scalars": [5]}])),
+        ("retrieval", seg(5, 3, 2, ("g",), [{"scalars": [1], "bounds": [1, 3, 5], "refs": [[], [0]]},
+                                            {"scalars": [0], "bounds": [0, 2, 3, 5], "refs": [[], [], [0]]}])),
+    ]
+
+
+@pytest.mark.parametrize("d,tiles", [(128, (128, 64, 128, 64)), (64, (64, 64, 64, 64))])
+def test_tiny_sequences_parity(d, tiles):
+    for i, (mask, md) in enumerate(tiny_sequences()):
+        print(f"[attention-tiny] {mask} N={md.N} d={d} tiles={tiles}", flush=True)
+        t = make_tensors(md.B, 2, md.N, d, 40 + i)
+        out = run_gpu(specs.BY_MASK[mask], md, t, tiles)
+        check_all(out, t, mask, md)
+        if mask == "causal":
+            check_all(run_gpu(None, md, t, tiles, causal=True), t, mask, md)
+
+
 def test_tiny_workload_parity():
     w = WORKLOADS["shared_prompt_tiny"]
     md = make_metadata(w)

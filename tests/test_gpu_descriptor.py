@@ -101,6 +101,17 @@ def test_small_ragged_cases_bit_exact(mask, N, tiles, seed):
     assert (desc.buffer[desc.bytes:].cpu().numpy() == 0xA5).all()
 
 
+@pytest.mark.parametrize("tiles", [(128, 64, 128, 64), (16, 80, 24, 8)])
+def test_tiny_sequences_bit_exact(tiles):
+    from tests.test_gpu_attention import tiny_sequences
+    for mask, md in tiny_sequences():
+        print(f"[descriptor-tiny] {mask} N={md.N} tiles={tiles}", flush=True)
+        words, desc, _ = gpu_descriptor(mask, md, tiles, guard_bytes=64)
+        want = od.build(mask, md, desc.K_r, desc.K_c, tiles)
+        assert np.array_equal(words, want), explain(words, want, md.B, md.N, desc.K_r, desc.K_c, tiles)
+        assert (desc.buffer[desc.bytes:].cpu().numpy() == 0xA5).all()
+
+
 def test_wide_columns_beyond_the_register_runs_use_the_memory_path():
     """Segment 0 referenced by every even segment (non-adjacent: separate runs)
     and segment 1 by every odd one: their key columns receive about 20
