@@ -124,7 +124,9 @@ typedef struct cm_metadata {
  * stride_n (all three 0 = contiguous [B,H,N,d]); lse is fp32 [B][H][N]
  * contiguous.  scale 0 means 1/sqrt(d).  causal = 1 selects the maskless
  * causal path (row i sees keys 0..i, tile states from indices, no descriptor:
- * desc may be NULL); causal = 0 uses the descriptor. */
+ * desc may be NULL); causal = 0 uses the descriptor.  Size limits (else
+ * CM_ERR_UNSUPPORTED): B * H * N <= 2^27 rows per call, and one head's rows,
+ * ((N - 1) * stride_n + d) bf16, span less than 4 GiB. */
 typedef struct cm_attn_args {
   int32_t B, H, N, d;
   int64_t stride_b, stride_h, stride_n;

@@ -133,6 +133,13 @@ cm_status check_attn(const cm_attn_args* args, const cm_desc* desc, AttnDims& di
     if (dims.sn < args->d || dims.sh < 1 || dims.sb < 1 || dims.sn % 8 || dims.sh % 8 || dims.sb % 8)
       return fail(CM_ERR_INVALID, "strides must be positive multiples of 8 elements with stride_n >= d");
   }
+  // the largest grid (rowsum(dO * O), 16 lanes per row) has 16 * B * H * N
+  // work-items, which must stay below 2^32; each head's rows are addressed
+  // through one buffer descriptor, whose size field has 32 bits
+  if (int64_t(args->B) * args->H * args->N > (int64_t(1) << 27))
+    return fail(CM_ERR_UNSUPPORTED, "B * H * N must be at most 2^27 rows per call");
+  if (((int64_t(args->N) - 1) * dims.sn + args->d) * 2 > int64_t(UINT32_MAX))
+    return fail(CM_ERR_UNSUPPORTED, "one head's rows ((N - 1) * stride_n + d bf16) must span less than 4 GiB");
   if (!std::isfinite(args->scale) || args->scale < 0) return fail(CM_ERR_INVALID, "scale must be finite and >= 0");
   dims.scale = args->scale == 0.f ? 1.0f / std::sqrt(float(args->d)) : args->scale;
   dims.causal = args->causal ? 1 : 0;

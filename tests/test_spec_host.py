@@ -186,6 +186,16 @@ def test_argument_checks_without_gpu():
     args = cm.cm_attn_args(1, 1, 128, 64, 0, 0, 0, 0.0, 1, 2)
     st = cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None)
     assert st == -2  # no such partial-tile check
+    # size limits: at most 2^27 rows per call, one head's rows within 4 GiB
+    args = cm.cm_attn_args(1 << 7, 1 << 4, (1 << 16) + 1, 128, 0, 0, 0, 0.0, 1)
+    assert cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None) == -5
+    args = cm.cm_attn_args(1, 1, 1 << 20, 128, 1 << 40, 1 << 40, 4096, 0.0, 1)
+    assert cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None) == -5
+    # just inside both limits: the size checks pass, the missing q is reported
+    args = cm.cm_attn_args(1, 1, 1 << 20, 128, 1 << 40, 1 << 40, 2048, 0.0, 1)
+    assert cm.library().cm_attn_fwd(args, None, 16, 16, None, 16, 16, None) == -1
+    args = cm.cm_attn_args(1 << 7, 1 << 4, 1 << 16, 128, 0, 0, 0, 0.0, 1)
+    assert cm.library().cm_attn_fwd(args, None, 16, 16, None, 16, 16, None) == -1
     assert cm.cm_status_str(-4) == "descriptor/spec/argument mismatch"
 
 
