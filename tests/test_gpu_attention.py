@@ -245,6 +245,49 @@ def test_forward_bitwise_repeatable_and_desc_reuse():
         assert torch.equal(a[n], b[n]), n
 
 
+def _busy(stream_cycles):
+    """Keep the current stream busy for a while (spin kernel, else matmuls)."""
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(stream_cycles)
+        return
+    a = torch.full((2048, 2048), 1e-3, device="cuda")
+    for _ in range(40):
+        a = a @ a
+
+
+def test_launches_follow_the_callers_stream():
+    """Every call enqueues on the stream it is given (here torch's current
+    stream inside a side-stream context, as the binding passes it): inputs
+    that the side stream writes only after a delay are the ones read, and
+    the outputs equal a default-stream run bit for bit."""
+    mask, N, d, tiles = "shared_prompt", 900, 128, (128, 64, 128, 64)
+    md = small_md(mask, N=N, seed=21, B=2)
+    t = make_tensors(2, 2, N, d, 21)
+    ref = run_gpu(specs.BY_MASK[mask], md, t, tiles)
+    src = {n: t[n].cuda() for n in ("q", "k", "v", "do")}
+    x = {n: torch.zeros_like(a) for n, a in src.items()}
+    spec = cm.cm_spec_compile(specs.BY_MASK[mask])
+    desc = cm.Descriptor(spec, 2, N, md.seg_cap, tiles)
+    dmd = cm.device_metadata(md)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        _busy(100_000_000)
+        for n in x:
+            x[n].copy_(src[n])
+        cm.cm_build_descriptor(spec, dmd, desc)
+        args = cm.attn_args(x["q"])
+        o = torch.empty_like(x["q"])
+        lse = torch.empty(2, 2, N, dtype=torch.float32, device="cuda")
+        cm.cm_attn_fwd(args, x["q"], x["k"], x["v"], desc, o, lse)
+        dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
+        ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device="cuda")
+        cm.cm_attn_bwd(args, x["q"], x["k"], x["v"], o, lse, x["do"], desc, dq, dk, dv, ws)
+    side.synchronize()
+    for n, got in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items():
+        assert torch.equal(got.cpu(), ref[n]), n
+
+
 def test_argument_errors_launch_nothing():
     spec = cm.cm_spec_compile(specs.CAUSAL)
     md = small_md("causal", N=256, B=1)
