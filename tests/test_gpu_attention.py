@@ -288,6 +288,54 @@ def test_launches_follow_the_callers_stream():
         assert torch.equal(got.cpu(), ref[n]), n
 
 
+def test_step_captured_in_a_hip_graph_replays_with_new_metadata():
+    """Descriptor build, forward and backward captured once into a HIP graph
+    (the hot calls allocate, copy and clear nothing) and replayed with new
+    metadata written into the same device buffers: every replay equals the
+    eager step on that metadata bit for bit, with eager work and
+    synchronisation between the replays."""
+    mask, N, d, tiles = "hstu", 1000, 128, (128, 64, 128, 64)
+    mds = [small_md(mask, N=N, seed=s, B=2) for s in (31, 32, 33)]
+    t = make_tensors(2, 2, N, d, 31)
+    eager = [run_gpu(specs.BY_MASK[mask], md, t, tiles) for md in mds]
+    spec = cm.cm_spec_compile(specs.BY_MASK[mask])
+    desc = cm.Descriptor(spec, 2, N, mds[0].seg_cap, tiles)
+    dmd = cm.device_metadata(mds[0])
+    x = {n: t[n].cuda() for n in ("q", "k", "v", "do")}
+    args = cm.attn_args(x["q"])
+    out = dict(o=torch.empty_like(x["q"]), lse=torch.empty(2, 2, N, dtype=torch.float32, device="cuda"),
+               dq=torch.empty_like(x["q"]), dk=torch.empty_like(x["q"]), dv=torch.empty_like(x["q"]))
+    ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device="cuda")
+
+    def step():
+        cm.cm_build_descriptor(spec, dmd, desc)
+        cm.cm_attn_fwd(args, x["q"], x["k"], x["v"], desc, out["o"], out["lse"])
+        cm.cm_attn_bwd(args, x["q"], x["k"], x["v"], out["o"], out["lse"], x["do"], desc,
+                       out["dq"], out["dk"], out["dv"], ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(2):
+        for i, (md, want) in enumerate(zip(mds, eager)):
+            print(f"[graph] replay {rep}.{i}", flush=True)
+            for name in ("scalars", "seg_bounds", "n_seg", "refs"):
+                dev = getattr(dmd, name)
+                if dev is not None:
+                    dev.copy_(torch.as_tensor(getattr(md, name), dtype=torch.int32).reshape(dev.shape))
+            g.replay()
+            torch.cuda.synchronize()
+            for n, got in out.items():
+                assert torch.equal(got.cpu(), want[n]), (rep, i, n)
+            run_gpu(specs.BY_MASK[mask], mds[(i + 1) % 3], t, tiles)  # eager work between replays
+
+
 def test_argument_errors_launch_nothing():
     spec = cm.cm_spec_compile(specs.CAUSAL)
     md = small_md("causal", N=256, B=1)
