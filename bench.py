@@ -201,6 +201,8 @@ def main():
     ap.add_argument("--specialize", action="store_true",
                     help="also time the preprocess of every workload with the interpreting kernel and with the "
                          "spec-specialised one (cm_spec_specialize); JSON lines to stderr")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time every workload's step eagerly and as a HIP graph replay; JSON lines to stderr")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the plain copy for counter scaling")
     ap.add_argument("--record-traffic", metavar="DIR", help="write profiles/traffic.json from counter runs in DIR")
     a = ap.parse_args()
@@ -236,6 +238,9 @@ def main():
                    "reduction": round(1.0 - base["ms_per_step"] / abl["ms_per_step"], 4),
                    "unsigned_kernel_ms": base["kernel_ms"], "ordinary_masked_kernel_ms": abl["kernel_ms"]}
             print("[bench-ablation] " + json.dumps(rec), file=sys.stderr, flush=True)
+    if a.graph:
+        for name in WORKLOADS:
+            print("[bench-graph] " + json.dumps(time_graph(name, a.steps, a.warmup)), file=sys.stderr, flush=True)
     if a.specialize:
         for name in WORKLOADS:
             print("[bench-specialize] " + json.dumps(time_preprocess(name, a.steps)), file=sys.stderr, flush=True)
@@ -287,6 +292,61 @@ def time_preprocess(name: str, steps: int) -> dict:
         torch.cuda.synchronize()
         out[kind + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
     return out
+
+
+def time_graph(name: str, steps: int, warmup: int) -> dict:
+    """One whole step (descriptor build, forward, backward) timed eagerly and
+    as a replay of a HIP graph captured once; milliseconds per step."""
+    import torch
+
+    import runtime_metadata_attention_amd as cm
+    from runtime_metadata_attention_amd import specs
+    from workloads import WORKLOADS, make_metadata, make_tensors
+
+    w = WORKLOADS[name]
+    md = make_metadata(w)
+    dev = torch.device("cuda", 0)
+    t = make_tensors(w.B, w.H, w.N, w.d, w.seed)
+    q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
+    del t
+    spec = cm.cm_spec_compile(specs.BY_MASK[w.mask])
+    desc = cm.Descriptor(spec, w.B, w.N, w.seg_cap, w.tiles, dev, packed=md.B if w.packed else 0)
+    dmd = cm.device_metadata(md, dev)
+    args = cm.attn_args(q)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device=dev)
+
+    def step():
+        cm.cm_build_descriptor(spec, dmd, desc)
+        cm.cm_attn_fwd(args, q, k, v, desc, o, lse)
+        cm.cm_attn_bwd(args, q, k, v, o, lse, do, desc, dq, dk, dv, ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    eager = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    graph = timed(g.replay)
+    return {"workload": name, "eager_ms": round(eager, 4), "graph_ms": round(graph, 4),
+            "saved": round(1.0 - graph / eager, 4)}
 
 
 def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool, check: int = 0,
