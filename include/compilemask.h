@@ -222,8 +222,9 @@ cm_status cm_desc_offsets(const cm_desc* desc, size_t* offsets);
  * compile-time constant, compiles it with hipRTC for gfx950 (about a second)
  * and loads it on the current device; from then on cm_build_descriptor with
  * this spec on that device launches it instead of the interpreting kernel.
- * The descriptor is bit-identical.  Synchronous, host side; call once per
- * spec and device.  The modules are unloaded by cm_spec_free.  CM_ERR_HIP
+ * The descriptor is bit-identical.  Synchronous, host side; a repeated call
+ * for the same device returns at once.  Threads may call it, and use the spec
+ * in other calls, concurrently.  The modules are unloaded by cm_spec_free.  CM_ERR_HIP
  * (with the compiler log in cm_last_error) if hipRTC or the loader fails.
  * cm_spec_codegen returns the generated source (same conventions as
  * cm_spec_dump). */

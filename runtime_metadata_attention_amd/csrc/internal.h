@@ -3,6 +3,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -30,6 +31,7 @@ struct cm_spec {
     void* function;              // hipFunction_t
   };
   std::vector<Specialized> specialized;
+  mutable std::mutex specialized_mu;  // guards `specialized` (the rest never changes)
   ~cm_spec();
 };
 

@@ -35,13 +35,17 @@ std::string specialized_source(const cm_spec* spec) {
   return s;
 }
 
-void* specialized_function(const cm_spec* spec) {
-  if (spec->specialized.empty()) return nullptr;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+static void* find_specialized(const cm_spec* spec, int dev) {
   for (const auto& x : spec->specialized)
     if (x.device == dev) return x.function;
   return nullptr;
+}
+
+void* specialized_function(const cm_spec* spec) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(spec->specialized_mu);
+  return find_specialized(spec, dev);
 }
 
 hipError_t launch_specialized(void* function, const PreprocessArgs& a, hipStream_t stream) {
@@ -84,6 +88,8 @@ cm_status cm_spec_specialize(cm_spec* spec) {
   hipError_t he = hipGetDevice(&dev);
   if (he != hipSuccess) return fail(CM_ERR_HIP, std::string("cm_spec_specialize: ") + hipGetErrorString(he));
   if (specialized_function(spec)) return CM_OK;
+  // compiled without the lock (about a second); a second caller that raced
+  // this one for the same device keeps the first module and drops its own
   const std::string src = specialized_source(spec);
   hiprtcProgram prog;
   hiprtcResult r = hiprtcCreateProgram(&prog, src.c_str(), "cm_preprocess_specialized.hip", kRtcHeaderCount,
@@ -114,7 +120,14 @@ cm_status cm_spec_specialize(cm_spec* spec) {
     (void)hipModuleUnload(module);
     return fail(CM_ERR_HIP, std::string("hipModuleGetFunction: ") + hipGetErrorString(he));
   }
-  spec->specialized.push_back({dev, module, function});
+  {
+    std::lock_guard<std::mutex> lock(spec->specialized_mu);
+    if (!find_specialized(spec, dev)) {
+      spec->specialized.push_back({dev, module, function});
+      return CM_OK;
+    }
+  }
+  (void)hipModuleUnload(module);
   return CM_OK;
 }
 

@@ -73,3 +73,46 @@ def test_specialised_full_size_bit_exact(name):
     print(f"[specialise-full] {name}", flush=True)
     words, desc, _ = gpu_descriptor(w.mask, md, w.tiles, spec=specialised(w.mask))
     assert hashlib.sha256(words.tobytes()).hexdigest() == gold["sha256"]
+
+
+def test_concurrent_specialise_and_build_on_one_spec():
+    """Two threads specialise one spec while a third keeps building
+    descriptors with it: one module is kept, and every descriptor (from the
+    interpreting or the specialised kernel) is the oracle's."""
+    import threading
+
+    mask, N, tiles = "shared_prompt", 900, (128, 64, 128, 64)
+    md = small_md(mask, N=N, seed=41, B=2)
+    spec = cm.cm_spec_compile(specs.BY_MASK[mask])
+    _, desc, _ = gpu_descriptor(mask, md, tiles, spec=spec)
+    want = od.build(mask, md, desc.K_r, desc.K_c, tiles)
+    errors, builds = [], []
+    done = threading.Event()
+
+    def specialise():
+        try:
+            cm.cm_spec_specialize(spec)
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(e)
+
+    def build():
+        try:
+            while not done.is_set() or not builds:
+                words, _, _ = gpu_descriptor(mask, md, tiles, spec=spec)
+                builds.append(np.array_equal(words, want))
+        except Exception as e:  # noqa: BLE001
+            errors.append(e)
+
+    workers = [threading.Thread(target=specialise), threading.Thread(target=specialise)]
+    builder = threading.Thread(target=build)
+    builder.start()
+    for t in workers:
+        t.start()
+    for t in workers:
+        t.join()
+    done.set()
+    builder.join()
+    assert not errors, errors
+    assert builds and all(builds)
+    words, _, _ = gpu_descriptor(mask, md, tiles, spec=spec)
+    assert np.array_equal(words, want)
