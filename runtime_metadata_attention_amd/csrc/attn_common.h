@@ -449,14 +449,23 @@ __device__ __forceinline__ void mask_pred(f32x16 (&s)[2], uint32_t base, int lan
 // tiles * hb work-groups (hb = samples x heads), ids are remapped so that
 // every (sample, head) is handled by one XCD (when hb is a multiple of 8):
 // the tiles of one head that run at the same time then stream the same
-// K/V (or Q/dO) tiles through the same L2.  Within a head, tiles are visited
-// in the order `tile_of(k)`, k = 0, 1, ...
+// K/V (or Q/dO) tiles through the same L2.  Each XCD holds hb / 8 heads;
+// it deals their tiles either tile by tile (`interleave`: tile k of every
+// head, then tile k + 1, ...) or head by head.  Tile k is the k-th in the
+// kernel's own order, which puts the longest tiles of lower-triangular masks
+// first: interleaving keeps every head's long tiles ahead of every head's
+// short ones.
 constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_coords(int w, int tiles, int hb, int& k, int& bh) {
+__device__ __forceinline__ void xcd_coords(int w, int tiles, int hb, bool interleave, int& k, int& bh) {
   if (hb % kXcds == 0) {
-    const int xcd = w % kXcds, local = w / kXcds;
-    bh = xcd + kXcds * (local / tiles);
-    k = local % tiles;
+    const int xcd = w % kXcds, local = w / kXcds, hpx = hb / kXcds;
+    if (interleave) {
+      bh = xcd + kXcds * (local % hpx);
+      k = local / hpx;
+    } else {
+      bh = xcd + kXcds * (local / tiles);
+      k = local % tiles;
+    }
   } else {
     bh = w / tiles;
     k = w % tiles;
