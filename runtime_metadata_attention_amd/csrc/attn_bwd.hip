@@ -163,11 +163,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lk = lane & 31;
   int kt, bh;
-  // first key tiles are seen by the most rows.  Heads are dealt tile by tile
-  // when they have few key tiles each; with many, head by head keeps the
-  // XCD's running work-groups on one head's Q/dO (measured: interleaving
-  // 256-tile heads costs 1%, interleaving 32- and 64-tile heads saves 5%).
-  xcd_coords(int(blockIdx.x), p.Tk_b, p.B * p.H, p.Tk_b < 128, kt, bh);
+  xcd_coords(int(blockIdx.x), p.Tk_b, p.B * p.H, p.Tk_b < kInterleaveBelow, kt, bh);  // first key tiles are seen by the most rows
   const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;
   const int k0 = kt * BK;
@@ -407,7 +403,7 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lq = lane & 31;
   int kx, bh;
-  xcd_coords(int(blockIdx.x), p.Tq_f, p.B * p.H, true, kx, bh);
+  xcd_coords(int(blockIdx.x), p.Tq_f, p.B * p.H, p.Tq_f < kInterleaveBelow, kx, bh);
   const int qt = p.Tq_f - 1 - kx;
   const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;

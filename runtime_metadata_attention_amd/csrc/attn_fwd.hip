@@ -57,7 +57,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   const int wave = int(uniform(uint32_t(tid >> 6)));  // wave-uniform by construction
   const int h = lane >> 5, lq = lane & 31;
   int kx, bh;
-  xcd_coords(int(blockIdx.x), p.Tq, p.B * p.H, true, kx, bh);
+  xcd_coords(int(blockIdx.x), p.Tq, p.B * p.H, p.Tq < kInterleaveBelow, kx, bh);
   const int qt = p.Tq - 1 - kx;  // the longest rows of lower-triangular masks first
   const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;
