@@ -10,7 +10,12 @@ Readings where the pages are silent:
   * lse is the natural-log log-sum-exp of the scaled visible scores;
   * a query row with no visible key has O = 0 and lse = -inf, its dQ row is 0
     and it adds nothing to dK or dV;
-  * the backward uses D = rowsum(dO * O) with the oracle's own float64 O.
+  * the backward uses D = rowsum(dO * O).  With the default stored_o=None, O
+    is the oracle's own float64 O (the exact gradient: D = rowsum(P * dP)).
+    With stored_o="bf16", O is that O rounded to bfloat16: the backward
+    entry point receives the forward's output `o`, which the library stores
+    in bf16, and computes D from it.  The parity tests compare against this
+    form; the exact form is what autograd and finite differences pin.
 
 Inputs are numpy or torch arrays [B, H, N, d] (bf16 values are upcast exactly).
 ``mask_rows(b, r0, r1)`` returns the boolean visibility of rows r0..r1-1
@@ -32,6 +37,23 @@ def _f64(x) -> np.ndarray:
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(x, np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (ties to even), via float32: keep the
+    upper 16 bits of the float32 pattern after adding 0x7FFF plus the lowest
+    kept bit (finite inputs)."""
+    bits = np.asarray(x, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _o_for_d(O, stored_o):
+    if stored_o is None:
+        return O
+    if stored_o == "bf16":
+        return round_bf16(O)
+    raise ValueError(f"stored_o must be None or 'bf16', not {stored_o!r}")
 
 
 def _scale(d: int, scale):
@@ -84,7 +106,7 @@ def probabilities(q, k, lse, M, scale=None):
     return P
 
 
-def backward_head(q, k, v, do, mask_rows, b: int, scale=None, block: int = 1024):
+def backward_head(q, k, v, do, mask_rows, b: int, scale=None, block: int = 1024, stored_o=None):
     """Analytic backward of one (b, h) pair; float64 [N, d] inputs.
 
     Returns dq, dk, dv (float64 [N, d]) and the forward O, lse it used.
@@ -92,7 +114,7 @@ def backward_head(q, k, v, do, mask_rows, b: int, scale=None, block: int = 1024)
     N, d = q.shape
     sc = _scale(d, scale)
     O, lse = forward_head(q, k, v, mask_rows, b, scale=scale, block=block)
-    Dvec = np.sum(do * O, axis=1)
+    Dvec = np.sum(do * _o_for_d(O, stored_o), axis=1)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -138,7 +160,7 @@ def forward(q, k, v, mask_rows, scale=None, block: int = 1024):
     return O, lse
 
 
-def backward(q, k, v, do, mask_rows, scale=None, block: int = 1024):
+def backward(q, k, v, do, mask_rows, scale=None, block: int = 1024, stored_o=None):
     """All heads: dq, dk, dv [B,H,N,d] (float64), plus O and lse."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
@@ -150,11 +172,11 @@ def backward(q, k, v, do, mask_rows, scale=None, block: int = 1024):
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h], O[b, h], lse[b, h] = backward_head(
-                q[b, h], k[b, h], v[b, h], do[b, h], mask_rows, b, scale=scale, block=block)
+                q[b, h], k[b, h], v[b, h], do[b, h], mask_rows, b, scale=scale, block=block, stored_o=stored_o)
     return dq, dk, dv, O, lse
 
 
-def sampled_head(q, k, v, do, mask_rows, b: int, rows, keys, scale=None, block: int = 1024):
+def sampled_head(q, k, v, do, mask_rows, b: int, rows, keys, scale=None, block: int = 1024, stored_o=None):
     """Full-size spot check of one (b, h) pair.
 
     Runs the whole forward (every row's lse and O are needed by the backward),
@@ -163,7 +185,7 @@ def sampled_head(q, k, v, do, mask_rows, b: int, rows, keys, scale=None, block: 
     N, d = q.shape
     sc = _scale(d, scale)
     O, lse = forward_head(q, k, v, mask_rows, b, scale=scale, block=block)
-    Dvec = np.sum(do * O, axis=1)
+    Dvec = np.sum(do * _o_for_d(O, stored_o), axis=1)
     rows = np.asarray(rows)
     keys = np.asarray(keys)
     # dq at the sampled rows

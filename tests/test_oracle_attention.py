@@ -167,3 +167,43 @@ def test_row_partition_sums_to_full_backward():
         sdv += pv
     np.testing.assert_allclose(sdk, dk, atol=1e-11)
     np.testing.assert_allclose(sdv, dv, atol=1e-11)
+
+
+def test_round_bf16_matches_torch_conversion():
+    """The oracle's bf16 rounding (ties to even, through float32) against
+    torch's float32 -> bfloat16 conversion, including exact ties."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4096) * 10.0 ** rng.integers(-4, 4, 4096),
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5 - 2.0 ** -7, 0.0, -0.0, 65504.0])])
+    x32 = x.astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oa.round_bf16(x32.astype(np.float64)), want)
+
+
+def test_stored_o_bf16_changes_only_d():
+    """stored_o="bf16" takes D from the bf16-rounded O.  When O is exactly a
+    bf16 value (one visible key per row: O = that key's bf16 v row), both
+    forms agree exactly; the sampled and the full backward agree with it on."""
+    N, d = 12, 16
+    rng = np.random.default_rng(6)
+    q, k, v, do = (oa._f64(torch_bf16(rng.standard_normal((1, 1, N, d)))) for _ in range(4))
+    fn = _mask_fn(np.eye(N, dtype=bool)[None])
+    a = oa.backward(q, k, v, do, fn)
+    b = oa.backward(q, k, v, do, fn, stored_o="bf16")
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    fn = _mask_fn(np.tril(np.ones((N, N), dtype=bool))[None])
+    full = oa.backward_head(q[0, 0], k[0, 0], v[0, 0], do[0, 0], fn, 0, stored_o="bf16")
+    s = oa.sampled_head(q[0, 0], k[0, 0], v[0, 0], do[0, 0], fn, 0, [0, 5, 11], [0, 7, 11], block=5, stored_o="bf16")
+    np.testing.assert_allclose(s["dq"], full[0][[0, 5, 11]], atol=1e-12)
+    np.testing.assert_allclose(s["dk"], full[1][[0, 7, 11]], atol=1e-12)
+    exact = oa.backward_head(q[0, 0], k[0, 0], v[0, 0], do[0, 0], fn, 0)
+    assert np.abs(exact[0] - full[0]).max() > 0  # the rounding of O does reach dq
+
+
+def torch_bf16(x):
+    import torch
+
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
