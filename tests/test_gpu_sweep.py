@@ -1,11 +1,18 @@
-"""Seeded sweep of small configurations against the oracle (GPU).
+"""Seeded sweep of small and medium configurations against the oracle (GPU).
 
 Each case draws from its own seed:
-* the mask family and N (1 to 700);
+* the mask family and N (1 to 700, or up to 4096 for the medium cases);
 * d (64 or 128), B and H (1 to 3);
 * tile shapes the attention kernels take;
 * a padded or a packed batch (packed: 1 to 4 samples, some of them empty);
 * contiguous or [B, N, H, d] storage.
+
+Mask proportions follow the workloads (see sample_md).  A key seen by every
+row with probability near 1/2 (HSTU with h = 1, a one-token prompt) would
+make bf16-rounded P add about 0.025 to that key's dV: beyond the 2e-2 bar
+for any kernel that rounds P to bf16, in a regime the workloads never reach
+(the degenerate h = 0 and h = 1 shapes are covered at N = 1 and 5 by the
+tiny-sequence tests).
 
 Descriptor words must equal the oracle's.  O, lse, dQ, dK and dV must meet
 the parity bars of test_gpu_attention.
@@ -19,8 +26,8 @@ from oracle import masks as om
 from tests.test_gpu_attention import check_all, run_gpu
 from tests.test_gpu_descriptor import explain, gpu_descriptor
 from tests.test_oracle_masks import small_md
-from tests.test_oracle_packed import packed_md
-from workloads import make_tensors
+from tests.test_oracle_packed import empty_sample
+from workloads import make_tensors, metadata_from_segments, pack_samples
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +35,35 @@ FAMILIES = ["causal", "hstu", "shared_prompt", "retrieval"]
 TILES = [(128, 64, 128, 64), (64, 64, 64, 64), (128, 64, 64, 64), (64, 64, 128, 64)]
 
 
-def draw_case(seed):
+def sample_md(mask, n, rng):
+    """One sample's metadata, with the proportions of the workloads: HSTU
+    h = max(1, floor(u n)), u ~ U[0.25, 0.94] (the packed HSTU workload's
+    rule); a prompt of at least n / 8 tokens (the reward workload's P is at
+    least 4096 of 32768); the retrieval family as the small oracle cases
+    draw it."""
+    if mask == "causal":
+        return metadata_from_segments(n, 0, 0, (), [{}])
+    if mask == "hstu":
+        return metadata_from_segments(n, 0, 0, ("h",), [{"scalars": [max(1, int(rng.uniform(0.25, 0.94) * n))]}])
+    if mask == "shared_prompt":
+        P = int(rng.integers(max(1, n // 8), max(2, n // 2)))
+        R = int(min(rng.integers(1, 6), n - P))
+        cuts = sorted(rng.choice(np.arange(P + 1, n), size=R - 1, replace=False).tolist()) if R > 1 else []
+        return metadata_from_segments(n, 8, 0, ("P",), [{"scalars": [P], "bounds": [P] + cuts + [n]}])
+    return small_md(mask, N=n, seed=int(rng.integers(1 << 30)), B=1)
+
+
+def batch_md(mask, n, B, rng):
+    samples = [sample_md(mask, n, rng) for _ in range(B)]
+    md = samples[0]
+    for x in samples[1:]:
+        for f in ("scalars", "seg_bounds", "n_seg", "refs"):
+            setattr(md, f, np.concatenate([getattr(md, f), getattr(x, f)]))
+    md.B = B
+    return md
+
+
+def draw_case(seed, n_max=700):
     rng = np.random.default_rng(10_000 + seed)
     mask = FAMILIES[int(rng.integers(len(FAMILIES)))]
     d = int(rng.choice([64, 128]))
@@ -38,20 +73,32 @@ def draw_case(seed):
     # families with segments need room for a prompt or prefix and a few segments
     lo = 2 if mask in ("causal", "hstu") else 64
     if rng.integers(3) == 0:
-        lengths = [int(rng.integers(lo, 300)) if rng.integers(4) else 0 for _ in range(int(rng.integers(1, 5)))]
+        lengths = [int(rng.integers(lo, max(lo + 1, n_max // 2))) if rng.integers(4) else 0
+                   for _ in range(int(rng.integers(1, 5)))]
         if sum(lengths) == 0:
             lengths[0] = lo
-        md = packed_md(mask, lengths, seed=seed)
+        md = pack_samples([sample_md(mask, n, rng) if n else empty_sample(mask, sample_md(mask, lo, rng))
+                           for n in lengths])
         B = 1
     else:
         B = int(rng.integers(1, 4))
-        md = small_md(mask, N=int(rng.integers(lo, 701)), seed=seed, B=B)
+        md = batch_md(mask, int(rng.integers(lo, n_max + 1)), B, rng)
     return mask, md, B, H, d, tiles, strided
 
 
 @pytest.mark.parametrize("seed", range(64))
 def test_random_small_configuration(seed):
-    mask, md, B, H, d, tiles, strided = draw_case(seed)
+    run_case(seed, *draw_case(seed))
+
+
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_random_medium_configuration(seed):
+    """Up to 4096 tokens: many tiles per row and column, and retrieval
+    columns with more runs than the kernels keep in registers."""
+    run_case(seed, *draw_case(seed, n_max=4096))
+
+
+def run_case(seed, mask, md, B, H, d, tiles, strided):
     packed = om.is_packed(md)
     print(f"[sweep] seed={seed} {mask} N={md.N} B={B} H={H} d={d} tiles={tiles} "
           f"packed={md.B if packed else 0} strided={strided}", flush=True)
