@@ -148,6 +148,20 @@ CM_HD bool eval_slot(const SampleView& s, const int32_t* p, int idx, int idx_seg
                      int32_t& lo_out, int32_t& hi_out) {
   const int hdr = p[0];
   const int n_lo = (hdr >> 4) & 15, n_hi = (hdr >> 8) & 15, n_conj = (hdr >> 12) & 15;
+  // the condition first: for most k an exists-slot's condition is false, and
+  // then its bounds need not be evaluated
+  if (n_conj > 0) {
+    const int32_t* q = p + 1 + kTermWords * (n_lo + n_hi);
+    bool any = false;
+    for (int c = 0; c < n_conj; ++c) {
+      const int na = q[0];
+      bool all = true;
+      for (int a = 0; a < na; ++a) all = all && eval_atom(s, q + 1 + kAtomWords * a, idx, idx_seg, k);
+      any = any || all;
+      q += 1 + kAtomWords * na;
+    }
+    if (!any) return false;
+  }
   const int32_t* q = p + 1;
   int64_t lo = 0, hi = s.N;
   bool ok = true;
@@ -160,17 +174,6 @@ CM_HD bool eval_slot(const SampleView& s, const int32_t* p, int idx, int idx_seg
     int64_t v;
     ok = ok && eval_term(s, q, idx, idx_seg, k, v);
     if (ok && v < hi) hi = v;
-  }
-  if (n_conj > 0) {
-    bool any = false;
-    for (int c = 0; c < n_conj; ++c) {
-      const int na = q[0];
-      bool all = true;
-      for (int a = 0; a < na; ++a) all = all && eval_atom(s, q + 1 + kAtomWords * a, idx, idx_seg, k);
-      any = any || all;
-      q += 1 + kAtomWords * na;
-    }
-    ok = ok && any;
   }
   if (hi > s.N) hi = s.N;
   if (lo < 0) lo = 0;
