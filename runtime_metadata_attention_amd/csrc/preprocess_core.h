@@ -120,8 +120,36 @@ __device__ __forceinline__ void runs_memory(const int32_t* prog, const Site& st,
     }
   }
   if (open) { row[nout++] = make_uint2(cs, ce); count_run(L, r, N, cs, ce); }
-  for (int q = nout; q < K; ++q) row[q] = make_uint2(0u, 0u);
+  // the rest of the row was cleared by the work-group (wide_table_clear);
+  // only the entries the sort used past the merged runs are stale
+  for (int q = nout; q < n; ++q) row[q] = make_uint2(0u, 0u);
   atomicMax(&L.misc[0], nout);
+}
+
+// An index of an invalid sample sees nothing: an all-zero row (wide rows
+// were cleared already).
+__device__ __forceinline__ void clear_row(const Role& r, int idx) {
+  if (r.K > 8) return;
+  uint2* row = r.table + size_t(idx) * r.K;
+  for (int t = 0; t < r.K; ++t) row[t] = make_uint2(0u, 0u);
+}
+
+// The runs of one index, by table width.
+__device__ __forceinline__ void build_runs(const int32_t* prog, const Site& st, const Role& r, const Lds& L, int N) {
+  if (r.K <= 1) runs_registers<1>(prog, st, r, L, N);
+  else if (r.K <= 2) runs_registers<2>(prog, st, r, L, N);
+  else if (r.K <= 4) runs_registers<4>(prog, st, r, L, N);
+  else if (r.K <= 8) runs_registers<8>(prog, st, r, L, N);
+  else runs_memory(prog, st, r, L, N);
+}
+
+// Clear the work-group's rows of a wide table (more than 8 entries per
+// index) with coalesced stores: the rows of consecutive indices are one
+// contiguous block.  Each index then writes only its runs.
+__device__ __forceinline__ void wide_table_clear(const Role& r) {
+  uint2* block = r.table + size_t(r.x0) * r.K;
+  const int total = r.nidx * r.K;
+  for (int t = threadIdx.x; t < total; t += kThreads) block[t] = make_uint2(0u, 0u);
 }
 
 // In-place inclusive prefix sums of a[0..T) and b[0..T) by one work-group.
@@ -201,6 +229,7 @@ __device__ __forceinline__ void preprocess_body(const PreprocessArgs& a, const i
   }
   for (int t = tid; t <= r.T; t += kThreads) { L.any[t] = 0; L.full[t] = 0; }
   if (tid == 0) { L.misc[0] = 0; L.misc[1] = 0; L.misc[2] = 0; L.misc[3] = 0; }
+  if (r.K > 8) wide_table_clear(r);  // ordered before the runs by the barriers below
   __syncthreads();
   if (packed) {
     // cu_seqlens must run from 0 to N without decreasing
@@ -238,46 +267,50 @@ __device__ __forceinline__ void preprocess_body(const PreprocessArgs& a, const i
 
   for (int q = tid; q < r.nidx; q += kThreads) {
     const int idx = r.x0 + q;
-    Site st;
-    st.global = idx;
-    bool skip;
+    // The runs are built in two branches with their own views, so that in
+    // the padded one the metadata pointers are known to be LDS (ds_read
+    // rather than flat loads, which cost several times more in the loops
+    // over segments).
     if (!packed) {
+      if (err != 0) {
+        clear_row(r, idx);
+        continue;
+      }
+      Site st;
+      st.global = idx;
       st.sv.N = a.N; st.sv.n_seg = n_seg; st.sv.n_refs = a.n_refs;
       st.sv.scalars = scal; st.sv.bounds = bounds; st.sv.refs = refs;
       st.local = idx;
       st.shift = 0;
-      skip = err != 0;
+      build_runs(prog, st, r, L, a.N);
     } else {
-      skip = cu_err != 0;
-      if (!skip) {
-        // the sample holding idx: the last one whose first token is <= idx
-        int lo = 0, hi = a.n_samples - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (a.cu_seqlens[mid] <= idx) lo = mid; else hi = mid - 1;
-        }
-        const int sb = lo, c0 = a.cu_seqlens[sb];
-        const int ns = a.n_seg ? a.n_seg[sb] : 0;
-        st.sv.N = a.cu_seqlens[sb + 1] - c0;
-        st.sv.n_seg = ns; st.sv.n_refs = a.n_refs;
-        st.sv.scalars = a.scalars ? a.scalars + size_t(sb) * a.n_scalars : nullptr;
-        st.sv.bounds = a.seg_bounds ? a.seg_bounds + size_t(sb) * (a.seg_cap + 1) : nullptr;
-        st.sv.refs = a.refs ? a.refs + size_t(sb) * a.seg_cap * a.n_refs : nullptr;
-        st.local = idx - c0;
-        st.shift = uint32_t(c0);
-        skip = validate_sample(st.sv.N, ns, a.seg_cap, st.sv.bounds, st.sv.refs, a.n_refs) != 0;
+      if (cu_err != 0) {
+        clear_row(r, idx);
+        continue;
       }
+      // the sample holding idx: the last one whose first token is <= idx
+      int lo = 0, hi = a.n_samples - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cu_seqlens[mid] <= idx) lo = mid; else hi = mid - 1;
+      }
+      const int sb = lo, c0 = a.cu_seqlens[sb];
+      const int ns = a.n_seg ? a.n_seg[sb] : 0;
+      Site st;
+      st.global = idx;
+      st.sv.N = a.cu_seqlens[sb + 1] - c0;
+      st.sv.n_seg = ns; st.sv.n_refs = a.n_refs;
+      st.sv.scalars = a.scalars ? a.scalars + size_t(sb) * a.n_scalars : nullptr;
+      st.sv.bounds = a.seg_bounds ? a.seg_bounds + size_t(sb) * (a.seg_cap + 1) : nullptr;
+      st.sv.refs = a.refs ? a.refs + size_t(sb) * a.seg_cap * a.n_refs : nullptr;
+      st.local = idx - c0;
+      st.shift = uint32_t(c0);
+      if (validate_sample(st.sv.N, ns, a.seg_cap, st.sv.bounds, st.sv.refs, a.n_refs) != 0) {
+        clear_row(r, idx);
+        continue;
+      }
+      build_runs(prog, st, r, L, a.N);
     }
-    if (skip) {
-      uint2* row = r.table + size_t(idx) * r.K;
-      for (int t = 0; t < r.K; ++t) row[t] = make_uint2(0u, 0u);
-      continue;
-    }
-    if (r.K <= 1) runs_registers<1>(prog, st, r, L, a.N);
-    else if (r.K <= 2) runs_registers<2>(prog, st, r, L, a.N);
-    else if (r.K <= 4) runs_registers<4>(prog, st, r, L, a.N);
-    else if (r.K <= 8) runs_registers<8>(prog, st, r, L, a.N);
-    else runs_memory(prog, st, r, L, a.N);
   }
   __syncthreads();
   scan2(L.any, L.full, r.T, part);
