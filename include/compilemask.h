@@ -135,18 +135,24 @@ typedef struct cm_attn_args {
   int32_t check;   /* partial-tile visibility check, CM_CHECK_*; 0 = the default */
 } cm_attn_args;
 
-/* Partial-tile visibility checks (cm_attn_args.check).  Both give identical
+/* Partial-tile visibility checks (cm_attn_args.check).  All give identical
  * results; they differ only in the instructions the kernels spend on it.
+ *   CM_CHECK_RUN_BITS (the default): per partial tile, each visible run's
+ *     endpoints are compared once against the tile's index range, giving
+ *     the range of the lane's elements the run covers; the ranges form one
+ *     visibility word, and each element costs a bit extract and a bit
+ *     select, however many runs the row or column has.
  *   CM_CHECK_UNSIGNED: visible runs, one subtraction (hoisted per row) and one
- *     unsigned compare per run (paper summary, section 3.3.2).
+ *     unsigned compare per run and element (paper summary, section 3.3.2).
  *   CM_CHECK_ORDINARY_MASKED: the ablation of section 4.4 / Table 3 there:
  *     masked intervals (the complement of the visible runs) with two ordinary
  *     compares and their conjunction per interval.  For measurement only. */
-#define CM_CHECK_UNSIGNED 0
+#define CM_CHECK_RUN_BITS 0
 #define CM_CHECK_ORDINARY_MASKED 1
 /*   CM_CHECK_PREDICATE: the predicate baseline (see cm_build_blockmask); the
  *     descriptor must come from cm_build_blockmask. */
 #define CM_CHECK_PREDICATE 2
+#define CM_CHECK_UNSIGNED 3
 
 /* ---- offline: MaskSpec -> symbolic endpoints (section 3.2.2) ------------ */
 

@@ -59,9 +59,10 @@ class cm_attn_args(ctypes.Structure):
                 ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("check", ctypes.c_int32)]
 
 
-CM_CHECK_UNSIGNED = 0
+CM_CHECK_RUN_BITS = 0
 CM_CHECK_ORDINARY_MASKED = 1
 CM_CHECK_PREDICATE = 2
+CM_CHECK_UNSIGNED = 3
 # predicate-baseline families (cm_build_blockmask)
 CM_PRED = {"causal": 0, "hstu": 1, "shared_prompt": 2, "retrieval": 3}
 
@@ -327,9 +328,9 @@ def cm_build_descriptor(spec: Spec, md: DeviceMetadata, desc: Descriptor, stream
 
 # ------------------------------------------------------------------ attention
 
-def attn_args(q, causal: bool = False, scale: float = 0.0, check: int = CM_CHECK_UNSIGNED) -> cm_attn_args:
+def attn_args(q, causal: bool = False, scale: float = 0.0, check: int = CM_CHECK_RUN_BITS) -> cm_attn_args:
     """cm_attn_args from a [B, H, N, d] bf16 tensor's shape and strides; `check` selects the partial-tile
-    visibility check (CM_CHECK_ORDINARY_MASKED is the ablation kernel)."""
+    visibility check (CM_CHECK_UNSIGNED and CM_CHECK_ORDINARY_MASKED are the ablation kernels)."""
     B, H, N, d = q.shape
     sb, sh, sn, sd = q.stride()
     if sd != 1:

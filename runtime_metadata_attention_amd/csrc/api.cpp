@@ -143,8 +143,10 @@ cm_status check_attn(const cm_attn_args* args, const cm_desc* desc, AttnDims& di
   if (!std::isfinite(args->scale) || args->scale < 0) return fail(CM_ERR_INVALID, "scale must be finite and >= 0");
   dims.scale = args->scale == 0.f ? 1.0f / std::sqrt(float(args->d)) : args->scale;
   dims.causal = args->causal ? 1 : 0;
-  if (args->check != CM_CHECK_UNSIGNED && args->check != CM_CHECK_ORDINARY_MASKED && args->check != CM_CHECK_PREDICATE)
-    return fail(CM_ERR_INVALID, "check must be CM_CHECK_UNSIGNED (0), CM_CHECK_ORDINARY_MASKED (1) or CM_CHECK_PREDICATE (2)");
+  if (args->check != CM_CHECK_RUN_BITS && args->check != CM_CHECK_ORDINARY_MASKED && args->check != CM_CHECK_PREDICATE &&
+      args->check != CM_CHECK_UNSIGNED)
+    return fail(CM_ERR_INVALID, "check must be CM_CHECK_RUN_BITS (0), CM_CHECK_ORDINARY_MASKED (1), CM_CHECK_PREDICATE (2) "
+                                "or CM_CHECK_UNSIGNED (3)");
   dims.check = args->check;
   if (args->check == CM_CHECK_PREDICATE && dims.causal)
     return fail(CM_ERR_INVALID, "the predicate baseline runs on a block-mask descriptor, not the maskless causal path");

@@ -639,7 +639,8 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dvv);
   dim3 grid(p.Tk_b * a.H * a.B);
-  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate;
+  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate,
+             un = a.check == kCheckUnsigned;
 #define CM_DKDV(DD, BKK)                                                                                              \
   do {                                                                                                               \
     if (pr) {                                                                                                        \
@@ -647,9 +648,12 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
     } else if (o) {                                                                                                         \
       if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
       else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
-    } else {                                                                                                         \
+    } else if (un) { \
       if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckUnsigned>), grid, dim3(BKK * 2), 0, stream, p); \
       else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckUnsigned>), grid, dim3(BKK * 2), 0, stream, p); \
+    } else { \
+      if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckRunBits>), grid, dim3(BKK * 2), 0, stream, p); \
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckRunBits>), grid, dim3(BKK * 2), 0, stream, p); \
     }                                                                                                                \
   } while (0)
   if (a.d == 128) { if (dv.bk == 128) CM_DKDV(128, 128); else CM_DKDV(128, 64); }
@@ -670,7 +674,8 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
   p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dq = static_cast<uint16_t*>(dq);
   dim3 grid(p.Tq_f * a.H * a.B);
-  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate;
+  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate,
+             un = a.check == kCheckUnsigned;
 #define CM_DQ(DD, BMM)                                                                                              \
   do {                                                                                                             \
     if (pr) {                                                                                                      \
@@ -678,9 +683,12 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
     } else if (o) {                                                                                                       \
       if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
       else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
-    } else {                                                                                                       \
+    } else if (un) { \
       if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckUnsigned>), grid, dim3(BMM * 2), 0, stream, p); \
       else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckUnsigned>), grid, dim3(BMM * 2), 0, stream, p); \
+    } else { \
+      if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckRunBits>), grid, dim3(BMM * 2), 0, stream, p); \
+      else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckRunBits>), grid, dim3(BMM * 2), 0, stream, p); \
     }                                                                                                              \
   } while (0)
   if (a.d == 128) { if (dv.fq == 128) CM_DQ(128, 128); else CM_DQ(128, 64); }

@@ -167,17 +167,59 @@ __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
 // Partial-tile visibility checks.  A lane's interval data are loop-invariant
 // registers (LaneRuns); `base` is the tile's first index plus 4h, so element
 // e of the tile sits at index j = base + elem_offset(e).
+//   kCheckRunBits (the default): each visible run [start, start + length) is
+//     turned into a range of the lane's element numbers with a few endpoint
+//     compares per run and tile (elements ordered by index, so a run covers
+//     a contiguous range of them), the ranges are OR-ed into one 32-bit word,
+//     and each element then costs one bit extract and one bit select.  The
+//     per-element work no longer grows with the number of runs.
 //   kCheckUnsigned: the visible runs as (start, length); j is visible when
 //     (j - start) <u length for some run: one subtraction (hoisted) and one
-//     compare per run (CompileMask paper summary, section 3.3.2).
+//     compare per run and element (CompileMask paper summary, section 3.3.2).
 //   kCheckOrdinaryMasked: the ablation the paper summary compares against
 //     (section 4.4, Table 3): the complement of the visible runs as masked
 //     intervals [lo, hi), and j is masked when lo <= j and j < hi for some
 //     interval: two compares and their conjunction per interval.
 // Invisible elements become `fill` (-inf for scores before a softmax, 0 for
 // probabilities).
-constexpr int kCheckUnsigned = 0;
+constexpr int kCheckRunBits = 0;
 constexpr int kCheckOrdinaryMasked = 1;
+constexpr int kCheckUnsigned = 3;
+
+// How many of a lane's 32 tile elements have an index below x.  The
+// elements sit at base + 8k + i (k = 0..7, i = 0..3), so with y = x - base
+// clamped to [0, 64] the count is 4 floor(y / 8) + min(y mod 8, 4).  (x and
+// base are at most N + 63 < 2^31, so the signed difference is exact.)
+__device__ __forceinline__ uint32_t elems_below(uint32_t x, uint32_t base) {
+  const int y = min(max(int(x - base), 0), 64);
+  return uint32_t(((y >> 3) << 2) + min(y & 7, 4));
+}
+
+// Bits [lo, hi) of a 32-bit word, 0 <= lo <= hi <= 32.
+__device__ __forceinline__ uint32_t bit_range(uint32_t lo, uint32_t hi) {
+  const uint32_t w = hi - lo;
+  return w >= 32u ? 0xFFFFFFFFu : (((1u << w) - 1u) << (lo & 31u));
+}
+
+// Bits of the lane's elements inside the run [start, start + len).
+__device__ __forceinline__ uint32_t run_bits(uint32_t start, uint32_t len, uint32_t base) {
+  return bit_range(elems_below(start, base), elems_below(start + len, base));
+}
+
+// Keep the elements whose bit is set, the others become fill: per element a
+// sign-extended one-bit extract (all ones or zero) and a bit select.
+__device__ __forceinline__ void apply_bits(f32x16 (&s)[2], uint32_t bits, float fill) {
+  const uint32_t f = __builtin_bit_cast(uint32_t, fill);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const uint32_t m = uint32_t(int32_t(bits << (31 - e)) >> 31);
+    // (the element goes through a scalar first: clang's __builtin_bit_cast
+    // applied directly to a vector subscript reads element 0)
+    const float sv = s[e >> 4][e & 15];
+    const uint32_t x = __builtin_bit_cast(uint32_t, sv);
+    s[e >> 4][e & 15] = __builtin_bit_cast(float, (x & m) | (f & ~m));
+  }
+}
 
 // A lane's first MAXR visible runs as (start, length); absent runs are
 // (0, 0) and only follow present ones.
@@ -190,7 +232,12 @@ struct LaneRuns {
 // of the tile's rows or columns is among them).
 template <int NR, int CHK, int MAXR>
 __device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const LaneRuns<MAXR>& lr, float fill) {
-  if (CHK == kCheckUnsigned) {
+  if (CHK == kCheckRunBits) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) bits |= run_bits(lr.a[r], lr.b[r], base);
+    apply_bits(s, bits, fill);
+  } else if (CHK == kCheckUnsigned) {
     uint32_t off[NR > 0 ? NR : 1];
 #pragma unroll
     for (int r = 0; r < NR; ++r) off[r] = base - lr.a[r];
@@ -240,7 +287,12 @@ template <int CHK>
 __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, const uint2* runs, int nr, bool valid,
                                               float fill) {
   uint32_t bits = 0;
-  if (CHK == kCheckUnsigned) {
+  if (CHK == kCheckRunBits) {
+    for (int r = 0; r < nr; ++r) {
+      const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
+      bits |= run_bits(rr.x, rr.y - rr.x, base);
+    }
+  } else if (CHK == kCheckUnsigned) {
     for (int r = 0; r < nr; ++r) {
       const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
       const uint32_t off = base - rr.x, len = rr.y - rr.x;
@@ -265,6 +317,10 @@ __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, con
 #pragma unroll
     for (int e = 0; e < 32; ++e) masked |= uint32_t(base + elem_offset(e >> 4, e & 15) >= prev) << e;
     bits = ~masked;
+  }
+  if (CHK == kCheckRunBits) {
+    apply_bits(s, bits, fill);
+    return;
   }
 #pragma unroll
   for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = ((bits >> e) & 1u) ? s[e >> 4][e & 15] : fill;

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     mfma_stream<D / 8, 4, 1>(
         [&](int i) { return lds_read_b128(cK + swz<D>((i & 1) * 32 + lq, 16 * (i >> 1) + 8 * h)); },
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
-    // partial tiles (and a ragged last tile): unsigned endpoint checks
+    // partial tiles (and a ragged last tile): endpoint checks against the row's runs
     if ((cs == 2) || ((ct + 1) * BN > N))
     {
       if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, -INFINITY);
@@ -219,7 +219,9 @@ hipError_t launch_dc(const FwdParams& p, bool causal, int check, hipStream_t str
   if (check == kCheckPredicate) return launch<D, BM, false, kCheckPredicate>(p, stream);
   if (check == kCheckOrdinaryMasked)
     return causal ? launch<D, BM, true, kCheckOrdinaryMasked>(p, stream) : launch<D, BM, false, kCheckOrdinaryMasked>(p, stream);
-  return causal ? launch<D, BM, true, kCheckUnsigned>(p, stream) : launch<D, BM, false, kCheckUnsigned>(p, stream);
+  if (check == kCheckUnsigned)
+    return causal ? launch<D, BM, true, kCheckUnsigned>(p, stream) : launch<D, BM, false, kCheckUnsigned>(p, stream);
+  return causal ? launch<D, BM, true, kCheckRunBits>(p, stream) : launch<D, BM, false, kCheckRunBits>(p, stream);
 }
 
 }  // namespace

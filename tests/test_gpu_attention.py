@@ -30,7 +30,7 @@ pytestmark = pytest.mark.gpu
 ATOL, RL2, LSE_ATOL = 2e-2, 1e-2, 1e-3
 
 
-def run_gpu(spec_text, md, t, tiles, causal=False, desc=None, spec=None, check=cm.CM_CHECK_UNSIGNED):
+def run_gpu(spec_text, md, t, tiles, causal=False, desc=None, spec=None, check=cm.CM_CHECK_RUN_BITS):
     """Build the descriptor (unless causal) and run forward + backward."""
     q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
     B, H, N, d = q.shape
@@ -197,9 +197,10 @@ ABLATION = [
 
 
 @pytest.mark.parametrize("mask,N,d,tiles,seed", ABLATION)
-def test_ordinary_masked_check_equals_unsigned_check_bitwise(mask, N, d, tiles, seed):
-    """The ablation kernels (ordinary compares on masked intervals) decide the
-    same visibility as the unsigned-check kernels, so every output is equal."""
+def test_ablation_checks_equal_the_default_check_bitwise(mask, N, d, tiles, seed):
+    """The per-element unsigned-compare kernels and the ablation kernels
+    (ordinary compares on masked intervals) decide the same visibility as the
+    default run-bitmask kernels, so every output is equal."""
     print(f"[ablation] {mask} N={N} d={d} tiles={tiles}", flush=True)
     if mask == "many_runs":
         md, mask = many_column_runs_md(N), "retrieval"
@@ -210,10 +211,11 @@ def test_ordinary_masked_check_equals_unsigned_check_bitwise(mask, N, d, tiles, 
         md = small_md(mask, N=N, seed=seed, B=2)
     t = make_tensors(md.B, 2, N, d, seed)
     a = run_gpu(specs.BY_MASK[mask], md, t, tiles)
-    b = run_gpu(specs.BY_MASK[mask], md, t, tiles, check=cm.CM_CHECK_ORDINARY_MASKED)
-    for n in ("o", "lse", "dq", "dk", "dv"):
-        assert torch.equal(a[n], b[n]), n
-    check_all(b, t, mask, md)
+    check_all(a, t, mask, md)
+    for check in (cm.CM_CHECK_UNSIGNED, cm.CM_CHECK_ORDINARY_MASKED):
+        b = run_gpu(specs.BY_MASK[mask], md, t, tiles, check=check)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            assert torch.equal(a[n], b[n]), (check, n)
 
 
 def test_columns_with_twenty_runs_parity():
@@ -229,14 +231,15 @@ def test_columns_with_twenty_runs_parity():
     check_all(out, t, "retrieval", md)
 
 
-def test_ordinary_masked_check_on_the_causal_path():
+def test_ablation_checks_on_the_causal_path():
     N = 700
     md = small_md("causal", N=N, B=1)
     t = make_tensors(1, 2, N, 128, 32)
     a = run_gpu(None, md, t, None, causal=True)
-    b = run_gpu(None, md, t, None, causal=True, check=cm.CM_CHECK_ORDINARY_MASKED)
-    for n in ("o", "lse", "dq", "dk", "dv"):
-        assert torch.equal(a[n], b[n]), n
+    for check in (cm.CM_CHECK_UNSIGNED, cm.CM_CHECK_ORDINARY_MASKED):
+        b = run_gpu(None, md, t, None, causal=True, check=check)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            assert torch.equal(a[n], b[n]), (check, n)
 
 
 def test_strided_layout_matches_contiguous():
