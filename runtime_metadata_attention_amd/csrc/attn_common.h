@@ -288,9 +288,14 @@ __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, con
                                               float fill) {
   uint32_t bits = 0;
   if (CHK == kCheckRunBits) {
-    for (int r = 0; r < nr; ++r) {
-      const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
-      bits |= run_bits(rr.x, rr.y - rr.x, base);
+    // four runs per round, their loads issued before any is used (entries
+    // between the lane's own run count and nr are zero-length padding)
+    for (int r = 0; r < nr; r += 4) {
+      uint2 rr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rr[t] = (valid && r + t < nr) ? runs[r + t] : make_uint2(0u, 0u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bits |= run_bits(rr[t].x, rr[t].y - rr[t].x, base);
     }
   } else if (CHK == kCheckUnsigned) {
     for (int r = 0; r < nr; ++r) {
