@@ -478,6 +478,19 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
       dma.issue(rV, sKV[buf ^ 1][1], uint32_t(tile) * tile_bytes);
     }
     const char* cur = lds0 + buf * (2 * TB);
+    buf ^= 1;
+
+    // partial and ragged tiles: with the run bitmask the visibility is known
+    // before the scores; a tile none of this wave's rows sees is skipped, one
+    // that all of them see entirely runs unmasked
+    const bool masked = (cs == 2) || ((ct + 1) * BN > N);
+    WaveTile wt;
+    wt.skip = false;
+    wt.select = masked;
+    if constexpr (CHK == kCheckRunBits) {
+      if (masked) wt.init(tile_bits<MAXR_Q>(uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid));
+    }
+    if (wt.skip) continue;
 
     // S^T = K Q^T (NS MFMAs), then dP^T = V dO^T (NS MFMAs) in eight fenced
     // chunks, each also computing four probabilities of the finished S^T
@@ -524,10 +537,10 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // partial and ragged tiles: invisible probabilities are zero
-    if ((cs == 2) || ((ct + 1) * BN > N))
-    {
+    // invisible probabilities are zero
+    if (wt.select) {
       if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, 0.f);
+      else if constexpr (CHK == kCheckRunBits) apply_bits(s, wt.bits, 0.f);
       else mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, 0.f);
     }
 
@@ -565,7 +578,6 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    buf ^= 1;
   }
 
   if (qvalid) {

@@ -281,6 +281,11 @@ __device__ __forceinline__ void mask_runs(f32x16 (&s)[2], uint32_t base, const L
   }
 }
 
+// Run-bitmask word from runs read from memory, four runs per round with
+// their loads issued before any is used (entries between the lane's own run
+// count and nr are zero-length padding).
+__device__ __forceinline__ uint32_t runs_bits_mem(uint32_t base, const uint2* runs, int nr, bool valid);
+
 // Same check with the runs read from memory (rows or columns with more runs
 // than the register copy holds).
 template <int CHK>
@@ -288,15 +293,7 @@ __device__ __forceinline__ void mask_runs_mem(f32x16 (&s)[2], uint32_t base, con
                                               float fill) {
   uint32_t bits = 0;
   if (CHK == kCheckRunBits) {
-    // four runs per round, their loads issued before any is used (entries
-    // between the lane's own run count and nr are zero-length padding)
-    for (int r = 0; r < nr; r += 4) {
-      uint2 rr[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) rr[t] = (valid && r + t < nr) ? runs[r + t] : make_uint2(0u, 0u);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bits |= run_bits(rr[t].x, rr[t].y - rr[t].x, base);
-    }
+    bits = runs_bits_mem(base, runs, nr, valid);
   } else if (CHK == kCheckUnsigned) {
     for (int r = 0; r < nr; ++r) {
       const uint2 rr = valid ? runs[r] : make_uint2(0u, 0u);
@@ -352,6 +349,63 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], uint32_t base, int nr,
     default: mask_runs_mem<CHK>(s, base, runs, nr, valid, fill); break;
   }
 }
+
+// The run-bitmask visibility word of one tile on its own, before any score
+// exists: the kernels test it across the wave first (a tile no row or column
+// of the wave sees is skipped; one that all of them see entirely needs no
+// select).  Same dispatch on the tile's run maximum as mask_tile.
+template <int NR, int MAXR>
+__device__ __forceinline__ uint32_t runs_bits(uint32_t base, const LaneRuns<MAXR>& lr) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) bits |= run_bits(lr.a[r], lr.b[r], base);
+  return bits;
+}
+
+__device__ __forceinline__ uint32_t runs_bits_mem(uint32_t base, const uint2* runs, int nr, bool valid) {
+  uint32_t bits = 0;
+  for (int r = 0; r < nr; r += 4) {
+    uint2 rr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rr[t] = (valid && r + t < nr) ? runs[r + t] : make_uint2(0u, 0u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bits |= run_bits(rr[t].x, rr[t].y - rr[t].x, base);
+  }
+  return bits;
+}
+
+template <int MAXR>
+__device__ __forceinline__ uint32_t tile_bits(uint32_t base, int nr, const LaneRuns<MAXR>& lr, const uint2* runs,
+                                              bool valid) {
+  static_assert(MAXR == 1 || MAXR == 2 || MAXR == 4, "register copy holds 1, 2 or 4 runs");
+  switch (nr) {
+    case 0: return 0u;
+    case 1: return runs_bits<1>(base, lr);
+    case 2:
+      if (MAXR >= 2) return runs_bits<(MAXR >= 2 ? 2 : 1)>(base, lr);
+      [[fallthrough]];
+    case 3:
+      if (MAXR >= 3) return runs_bits<(MAXR >= 3 ? 3 : 1)>(base, lr);
+      [[fallthrough]];
+    case 4:
+      if (MAXR >= 4) return runs_bits<(MAXR >= 4 ? 4 : 1)>(base, lr);
+      [[fallthrough]];
+    default: return runs_bits_mem(base, runs, nr, valid);
+  }
+}
+
+// What a wave does with a masked tile under the run bitmask: skip it (no
+// lane sees any element), run it unmasked (every lane sees every element),
+// or select per element.
+struct WaveTile {
+  uint32_t bits;
+  bool skip, select;
+  __device__ __forceinline__ void init(uint32_t b) {
+    bits = b;
+    skip = !__any(b != 0u);
+    select = !__all(b == 0xFFFFFFFFu);
+  }
+};
 
 // The lane's first MAXR runs from its interval-table row (the first `nr`
 // entries, nr being the tile's run maximum) or, on the maskless causal path,

@@ -126,16 +126,29 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     }
     const uint16_t* cK = sK[buf];
     const uint16_t* cV = sV[buf];
+    buf ^= 1;
+
+    // partial tiles (and a ragged last tile): endpoint checks against the
+    // row's runs.  With the run bitmask the visibility is known before the
+    // scores: a tile that none of this wave's rows sees is skipped, and one
+    // that all of them see entirely runs unmasked.
+    const bool masked = (cs == 2) || ((ct + 1) * BN > N);
+    WaveTile wt;
+    wt.skip = false;
+    wt.select = masked;
+    if constexpr (CHK == kCheckRunBits) {
+      if (masked) wt.init(tile_bits<MAXR>(uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid));
+    }
+    if (wt.skip) continue;
 
     // S^T = K Q^T for two 32-key blocks (operand reads pipelined ahead)
     f32x16 s[2] = {f32x16{}, f32x16{}};
     mfma_stream<D / 8, 4, 1>(
         [&](int i) { return lds_read_b128(cK + swz<D>((i & 1) * 32 + lq, 16 * (i >> 1) + 8 * h)); },
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
-    // partial tiles (and a ragged last tile): endpoint checks against the row's runs
-    if ((cs == 2) || ((ct + 1) * BN > N))
-    {
+    if (wt.select) {
       if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, -INFINITY);
+      else if constexpr (CHK == kCheckRunBits) apply_bits(s, wt.bits, -INFINITY);
       else mask_tile<CHK>(s, uint32_t(ct * BN + 4 * h), nr, runs, myruns, qvalid, -INFINITY);
     }
 
@@ -182,7 +195,6 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
           return cat4(lds_read_tr4(cV + swz<D>(kr, col)), lds_read_tr4(cV + swz<D>(kr + 8, col)));
         },
         [&](int i, const bf16x8& a) { acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]); });
-    buf ^= 1;
   }
 
   // epilogue: O = acc / l, lse = ln-sum-exp (natural log)
