@@ -257,12 +257,25 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     const float* cL = sL[buf];
     const float* cD = sD[buf];
 
+    // partial and ragged tiles: with the run bitmask the visibility is known
+    // before the scores.  A tile none of this wave's key columns sees leaves
+    // P = 0 without its S and dP MFMAs (its dS is then zero; the chunk phase
+    // still carries the previous tile's dV/dK); one that all of them see
+    // entirely runs unmasked.
+    const bool masked = (cs == 2) || ((ct + 1) * BQ > N);
+    WaveTile wt;
+    wt.skip = false;
+    wt.select = masked;
+    if constexpr (CHK == kCheckRunBits) {
+      if (masked) wt.init(tile_bits<MAXR>(uint32_t(ct * BQ + 4 * h), nr, runs, myruns, kvalid));
+    }
+
     // S = Q K^T (NS MFMAs), then dP = dO V^T (NS MFMAs) in eight fenced
     // chunks, each also computing four probabilities P = exp2(S log2e/sqrt(d)
     // - lse2) of the finished S (lane = key column; its lse2 rows are read
     // one chunk ahead).
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    {
+    if (!wt.skip) {
       constexpr int NS = D / 8, NM = 2 * NS, G = 4, MPC = NS / 8;
       auto rd = [&](int i) {
         const int j = i % NS;
@@ -307,10 +320,10 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // partial and ragged tiles: invisible probabilities are zero
-    if ((cs == 2) || ((ct + 1) * BQ > N))
-    {
+    // invisible probabilities are zero
+    if (wt.select && !wt.skip) {
       if constexpr (PRED) mask_pred<false>(s, uint32_t(ct * BQ + 4 * h), key, kvalid, ps, 0.f);
+      else if constexpr (CHK == kCheckRunBits) apply_bits(s, wt.bits, 0.f);
       else mask_tile<CHK>(s, uint32_t(ct * BQ + 4 * h), nr, runs, myruns, kvalid, 0.f);
     }
 
