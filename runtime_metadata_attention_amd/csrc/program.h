@@ -142,26 +142,48 @@ CM_HD int slot_words(const int32_t* p) {
   return w;
 }
 
-// Evaluate a slot for one value of the exists variable k.  Returns true and
-// [lo, hi) when the slot contributes a non-empty interval.
-CM_HD bool eval_slot(const SampleView& s, const int32_t* p, int idx, int idx_seg, int k,
-                     int32_t& lo_out, int32_t& hi_out) {
+// A slot's condition (a disjunction of conjunctions of atoms) for one value
+// of the exists variable k; true when the slot has none.
+CM_HD bool slot_cond(const SampleView& s, const int32_t* p, int idx, int idx_seg, int k) {
   const int hdr = p[0];
   const int n_lo = (hdr >> 4) & 15, n_hi = (hdr >> 8) & 15, n_conj = (hdr >> 12) & 15;
-  // the condition first: for most k an exists-slot's condition is false, and
-  // then its bounds need not be evaluated
-  if (n_conj > 0) {
-    const int32_t* q = p + 1 + kTermWords * (n_lo + n_hi);
-    bool any = false;
-    for (int c = 0; c < n_conj; ++c) {
-      const int na = q[0];
-      bool all = true;
-      for (int a = 0; a < na; ++a) all = all && eval_atom(s, q + 1 + kAtomWords * a, idx, idx_seg, k);
-      any = any || all;
-      q += 1 + kAtomWords * na;
-    }
-    if (!any) return false;
+  if (n_conj == 0) return true;
+  const int32_t* q = p + 1 + kTermWords * (n_lo + n_hi);
+  bool any = false;
+  for (int c = 0; c < n_conj; ++c) {
+    const int na = q[0];
+    bool all = true;
+    for (int a = 0; a < na; ++a) all = all && eval_atom(s, q + 1 + kAtomWords * a, idx, idx_seg, k);
+    any = any || all;
+    q += 1 + kAtomWords * na;
   }
+  return any;
+}
+// True when no term of the slot (bounds or condition) reads the index itself:
+// the slot then depends on the index only through the index's segment.
+CM_HD bool slot_index_free(const int32_t* p) {
+  const int hdr = p[0];
+  const int n_lo = (hdr >> 4) & 15, n_hi = (hdr >> 8) & 15, n_conj = (hdr >> 12) & 15;
+  const int32_t* q = p + 1;
+  for (int t = 0; t < n_lo + n_hi; ++t, q += kTermWords)
+    if ((q[0] & 7) == BK_IDX || ((q[0] >> 16) & 7) == BK_IDX) return false;
+  for (int c = 0; c < n_conj; ++c) {
+    const int na = q[0];
+    for (int a = 0; a < na; ++a) {
+      const int32_t* t = q + 1 + kAtomWords * a + 1;
+      if ((t[0] & 7) == BK_IDX || ((t[0] >> 16) & 7) == BK_IDX) return false;
+    }
+    q += 1 + kAtomWords * na;
+  }
+  return true;
+}
+
+// A slot's interval [lo, hi) for one value of the exists variable k, its
+// condition aside.  Returns true when the interval is non-empty.
+CM_HD bool slot_bounds(const SampleView& s, const int32_t* p, int idx, int idx_seg, int k,
+                       int32_t& lo_out, int32_t& hi_out) {
+  const int hdr = p[0];
+  const int n_lo = (hdr >> 4) & 15, n_hi = (hdr >> 8) & 15;
   const int32_t* q = p + 1;
   int64_t lo = 0, hi = s.N;
   bool ok = true;
@@ -182,6 +204,62 @@ CM_HD bool eval_slot(const SampleView& s, const int32_t* p, int idx, int idx_seg
   return ok && lo < hi;
 }
 
+// Evaluate a slot for one value of the exists variable k.  Returns true and
+// [lo, hi) when the slot contributes a non-empty interval.  The condition
+// comes first: for most k an exists-slot's condition is false, and then its
+// bounds need not be evaluated.
+CM_HD bool eval_slot(const SampleView& s, const int32_t* p, int idx, int idx_seg, int k,
+                     int32_t& lo_out, int32_t& hi_out) {
+  return slot_cond(s, p, idx, idx_seg, k) && slot_bounds(s, p, idx, idx_seg, k, lo_out, hi_out);
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// An exists-slot evaluated by the whole wave at once.  Each program word
+// read is a dependent scalar load, so the per-index loop over every k costs
+// a few hundred cycles per k.  When the slot does not read the index itself
+// and every active lane's index belongs to the same sample, the slot's
+// intervals depend on the lane only through its segment.  The wave then
+// takes the distinct segments of its lanes in turn: the active lane of rank
+// r (r-th active lane by lane id) evaluates the condition for
+// k = k0 + r, a ballot collects the k that hold, every lane evaluates the
+// bounds of just those (the same values on every lane), and the lanes of
+// that segment emit them, in ascending k as the per-index loop does.
+// Returns false (nothing emitted) when the wave does not qualify; the
+// caller then loops over k per index.
+template <class Emit>
+__device__ __forceinline__ bool exists_by_wave(const SampleView& s, const int32_t* p, int idx, int idx_seg,
+                                               Emit&& emit) {
+  if (!slot_index_free(p)) return false;  // program words: wave-uniform
+  const uint64_t active = __builtin_amdgcn_ballot_w64(true);
+  const uint64_t bp = (uint64_t)(const void*)s.bounds;
+  const uint32_t b_lo = __builtin_amdgcn_readfirstlane(uint32_t(bp)), b_hi = __builtin_amdgcn_readfirstlane(uint32_t(bp >> 32));
+  if (__builtin_amdgcn_ballot_w64(uint32_t(bp) == b_lo && uint32_t(bp >> 32) == b_hi) != active) return false;
+  // inactive lanes take no k: ranks count active lanes only
+  const int rank = int(__builtin_amdgcn_mbcnt_hi(uint32_t(active >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(active), 0u)));
+  const int n_active = __builtin_popcountll(active);
+  uint64_t todo = active;
+  while (todo != 0) {
+    const int leader = __builtin_ctzll(todo);
+    const int seg0 = __builtin_amdgcn_readlane(idx_seg, leader);
+    const bool mine = idx_seg == seg0;
+    todo &= ~__builtin_amdgcn_ballot_w64(mine);
+    for (int k0 = 0; k0 < s.n_seg; k0 += n_active) {
+      const int k = k0 + rank;
+      const bool c = k < s.n_seg && slot_cond(s, p, idx, seg0, k);
+      uint64_t m = __builtin_amdgcn_ballot_w64(c);
+      while (m != 0) {
+        const int lane = __builtin_ctzll(m);
+        const int kk = k0 + __builtin_popcountll(active & ((uint64_t(1) << lane) - 1));
+        m &= m - 1;
+        int32_t lo, hi;
+        if (slot_bounds(s, p, idx, seg0, kk, lo, hi) && mine) emit(lo, hi);
+      }
+    }
+  }
+  return true;
+}
+#endif
+
 // Walk one direction's regions for index idx and hand every non-empty slot
 // interval to emit(lo, hi).  Program words are read at offsets that depend
 // only on the program, so on the GPU every read is wave-uniform.
@@ -201,7 +279,11 @@ CM_HD void eval_direction(const int32_t* prog, int dir_off, const SampleView& s,
     for (int sl = 0; sl < n_slots; ++sl) {
       if (g) {
         if (p[0] & 1) {
-          for (int k = 0; k < s.n_seg; ++k) {
+          bool done = false;
+#if defined(__HIP_DEVICE_COMPILE__)
+          done = exists_by_wave(s, p, idx, idx_seg, emit);
+#endif
+          for (int k = 0; !done && k < s.n_seg; ++k) {
             int32_t lo, hi;
             if (eval_slot(s, p, idx, idx_seg, k, lo, hi)) emit(lo, hi);
           }
