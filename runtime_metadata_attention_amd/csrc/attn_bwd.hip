@@ -97,51 +97,6 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------ shared pieces
-
-// Per-lane byte offsets of the LDS operand reads inside one swizzled BR x D
-// tile (row-major, D bf16 per row).
-//   row[m]     : MFMA A-operand rows, ds_read_b128 of row (lane % 32), d chunk
-//                16 m + 8 h; the second 32-row block adds 32 D * 2 bytes.
-//   tr(db, hf) : transposed reads for the k-major operand of d block db: the
-//                address lane (g, gi) supplies for rows 8 hf + 4 (g / 2) +
-//                gi / 4, columns 32 db + 16 (g % 2) + 4 (gi % 4); each further
-//                16-row chunk adds 16 D * 2 bytes.
-// The swizzle only depends on the low four row bits, so the row-block and
-// 16-row offsets are immediates of the LDS instructions.
-// With COMPACT, the second half (hf = 1, eight rows further) is formed on the
-// fly: it differs from the first by a per-lane constant, since the swizzle of
-// rows 8..15 flips chunk bit 1, which for these lanes is g % 2 whatever db
-// is.  That saves D / 32 registers for one add per transposed pair.
-template <int D, bool COMPACT>
-struct LdsOffsets {
-  uint32_t row[D / 16];
-  uint32_t tr0[D / 32];
-  uint32_t tr1[COMPACT ? 1 : D / 32];
-  __device__ __forceinline__ void init(int lane) {
-    const int h = lane >> 5, lr = lane & 31, g = lane >> 4, gi = lane & 15;
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) row[m] = uint32_t(swz<D>(lr, 16 * m + 8 * h)) * 2u;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      tr0[db] = uint32_t(swz<D>(4 * (g >> 1) + (gi >> 2), db * 32 + 16 * (g & 1) + 4 * (gi & 3))) * 2u;
-      if (!COMPACT) tr1[db] = uint32_t(swz<D>(8 + 4 * (g >> 1) + (gi >> 2), db * 32 + 16 * (g & 1) + 4 * (gi & 3))) * 2u;
-    }
-    if (COMPACT) tr1[0] = uint32_t(swz<D>(8 + 4 * (g >> 1) + (gi >> 2), 16 * (g & 1) + 4 * (gi & 3))) * 2u - tr0[0];
-  }
-  __device__ __forceinline__ uint32_t tr(int db, int hf) const {
-    if (!hf) return tr0[db];
-    return COMPACT ? tr0[db] + tr1[0] : tr1[COMPACT ? 0 : db];
-  }
-};
-
-__device__ __forceinline__ bf16x8 lds_b128_at(const char* p) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
-}
-__device__ __forceinline__ bf16x8 lds_tr8_at(const char* p0, const char* p1) {
-  return cat4(lds_read_tr4(reinterpret_cast<const uint16_t*>(p0)), lds_read_tr4(reinterpret_cast<const uint16_t*>(p1)));
-}
-
 // ------------------------------------------------------------------ dK / dV
 
 template <int D, int BK, bool CAUSAL, int CHK>

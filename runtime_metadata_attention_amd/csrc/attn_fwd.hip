@@ -70,6 +70,10 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   TileDma<D, BN, NW> dma;
   dma.init(wave, lane, p.sn);
   const uint32_t tile_bytes = uint32_t(BN * p.sn * 2);
+  // per-lane byte offsets of the K row reads and V transposed reads; the
+  // 32-key block and 16-key chunk offsets are immediates
+  LdsOffsets<D, true> lo;
+  lo.init(lane);
 
   // Q^T as MFMA B operands: lane holds Q[q][16c + 8h .. +7]
   bf16x8 qreg[D / 16];
@@ -114,7 +118,6 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     dma.issue(rK, sK[0], uint32_t(tile) * tile_bytes);
     dma.issue(rV, sV[0], uint32_t(tile) * tile_bytes);
   }
-  const int g = lane >> 4, gi = lane & 15;
   while (have) {
     const int ct = tile, cs = state;
     have = next_tile(tile, state);
@@ -124,8 +127,8 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
       dma.issue(rK, sK[buf ^ 1], uint32_t(tile) * tile_bytes);
       dma.issue(rV, sV[buf ^ 1], uint32_t(tile) * tile_bytes);
     }
-    const uint16_t* cK = sK[buf];
-    const uint16_t* cV = sV[buf];
+    const char* cK = reinterpret_cast<const char*>(sK[buf]);
+    const char* cV = reinterpret_cast<const char*>(sV[buf]);
     buf ^= 1;
 
     // partial tiles (and a ragged last tile): endpoint checks against the
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     // S^T = K Q^T for two 32-key blocks (operand reads pipelined ahead)
     f32x16 s[2] = {f32x16{}, f32x16{}};
     mfma_stream<D / 8, 4, 1>(
-        [&](int i) { return lds_read_b128(cK + swz<D>((i & 1) * 32 + lq, 16 * (i >> 1) + 8 * h)); },
+        [&](int i) { return lds_b128_at(cK + (i & 1) * (32 * D * 2) + lo.row[i >> 1]); },
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
     if (wt.select) {
       if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, -INFINITY);
@@ -190,9 +193,8 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     mfma_stream<4 * (D / 32), 4, 2>(
         [&](int i) {
           const int kc = i / (D / 32), db = i % (D / 32);
-          const int kr = kc * 16 + 4 * (g >> 1) + (gi >> 2);
-          const int col = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          return cat4(lds_read_tr4(cV + swz<D>(kr, col)), lds_read_tr4(cV + swz<D>(kr + 8, col)));
+          const char* t = cV + kc * (16 * D * 2);
+          return lds_tr8_at(t + lo.tr(db, 0), t + lo.tr(db, 1));
         },
         [&](int i, const bf16x8& a) { acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]); });
   }
