@@ -203,7 +203,7 @@ __device__ __forceinline__ void mfma_stream(Read&& read, Mma&& mma) {
 
 // Offset, inside a 64-wide tile, of element v of 32-block blk of a score
 // tile in C layout, for the lane half h = 0 (add 4h for the other half).
-__device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
+__host__ __device__ __forceinline__ constexpr uint32_t elem_offset(int blk, int v) {
   return uint32_t(blk * 32 + (v >> 2) * 8 + (v & 3));
 }
 
@@ -233,19 +233,19 @@ constexpr int kCheckUnsigned = 3;
 // elements sit at base + 8k + i (k = 0..7, i = 0..3), so with y = x - base
 // clamped to [0, 64] the count is 4 floor(y / 8) + min(y mod 8, 4).  (x and
 // base are at most N + 63 < 2^31, so the signed difference is exact.)
-__device__ __forceinline__ uint32_t elems_below(uint32_t x, uint32_t base) {
+__host__ __device__ __forceinline__ uint32_t elems_below(uint32_t x, uint32_t base) {
   const int y = min(max(int(x - base), 0), 64);
   return uint32_t(((y >> 3) << 2) + min(y & 7, 4));
 }
 
 // Bits [lo, hi) of a 32-bit word, 0 <= lo <= hi <= 32.
-__device__ __forceinline__ uint32_t bit_range(uint32_t lo, uint32_t hi) {
+__host__ __device__ __forceinline__ uint32_t bit_range(uint32_t lo, uint32_t hi) {
   const uint32_t w = hi - lo;
   return w >= 32u ? 0xFFFFFFFFu : (((1u << w) - 1u) << (lo & 31u));
 }
 
 // Bits of the lane's elements inside the run [start, start + len).
-__device__ __forceinline__ uint32_t run_bits(uint32_t start, uint32_t len, uint32_t base) {
+__host__ __device__ __forceinline__ uint32_t run_bits(uint32_t start, uint32_t len, uint32_t base) {
   return bit_range(elems_below(start, base), elems_below(start + len, base));
 }
 

@@ -81,3 +81,18 @@ def test_c_driver_matches_python_binding(tmp_path):
     ref = run_gpu(specs.BY_MASK[mask], md, t, tiles, spec=spec, desc=desc)
     for name in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(outs[name], ref[name]), name
+
+
+def test_run_bitmask_matches_the_run_definition(tmp_path):
+    """The partial-tile run bitmask (per run and tile: two clamped element
+    counts and a bit range) against the element-by-element definition of a
+    run, exhaustively over runs [s, e) within 200 indices, every 64-wide
+    tile and both lane halves (tests/run_bits_check.cpp, host code)."""
+    exe = str(tmp_path / "run_bits_check")
+    src = os.path.join(ROOT, "tests", "run_bits_check.cpp")
+    cmd = [os.path.join(ROCM, "bin", "hipcc"), "-std=c++17", "-O1", "-x", "hip", "--cuda-host-only",
+           "-I", os.path.join(ROOT, "include"), src, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe, "200"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
