@@ -70,27 +70,39 @@ constexpr int BN = 64;  // keys per step of the dQ kernel
 
 // ------------------------------------------------------------------ D
 
+// Four lanes per row, each with D / 32 sixteen-byte chunks of O and dO in
+// flight (the chunks of one load instruction are 64 contiguous bytes of 16
+// rows); two exchanges finish the row sum.  Rows are at most 2^27 (an
+// argument check), so the index arithmetic is 32-bit.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;          // lanes per row
-  constexpr int RPB = 256 / LPR;      // rows per block
-  const int t = threadIdx.x;
-  const int64_t row = int64_t(blockIdx.x) * RPB + t / LPR;
-  const int64_t total = int64_t(p.B) * p.H * p.N;
+  constexpr int LPR = 4;             // lanes per row
+  constexpr int CPL = D / 8 / LPR;   // 16-byte chunks per lane
+  constexpr int RPB = 256 / LPR;     // rows per block
+  const int t = threadIdx.x, j = t % LPR;
+  const int row = int(blockIdx.x) * RPB + t / LPR;
+  const int total = p.B * p.H * p.N;
   float acc = 0.f;
   if (row < total) {
-    const int n = int(row % p.N);
-    const int64_t bh = row / p.N;
-    const int hh = int(bh % p.H), bb = int(bh / p.H);
-    const size_t off = size_t(bb) * p.sb + size_t(hh) * p.sh + size_t(n) * p.sn + (t % LPR) * 8;
-    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(p.o + off));
-    const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(p.dO + off));
+    const int n = row % p.N, bh = row / p.N;
+    const int hh = bh % p.H, bb = bh / p.H;
+    const size_t off = size_t(bb) * p.sb + size_t(hh) * p.sh + size_t(n) * p.sn + j * 8;
+    uint4 ua[CPL], ub[CPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += float(a[e]) * float(b[e]);
+    for (int c = 0; c < CPL; ++c) {
+      ua[c] = *reinterpret_cast<const uint4*>(p.o + off + c * (LPR * 8));
+      ub[c] = *reinterpret_cast<const uint4*>(p.dO + off + c * (LPR * 8));
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const bf16x8 a = as_bf16x8(ua[c]), b = as_bf16x8(ub[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(float(a[e]), float(b[e]), acc);
+    }
   }
-#pragma unroll
-  for (int s = LPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < total && (t % LPR) == 0) {
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 1, 64);
+  if (row < total && j == 0) {
     p.Dout[row] = acc;
     const float x = p.lse[row];
     p.lse2out[row] = (x == -INFINITY) ? INFINITY : x * kLog2e;
@@ -598,7 +610,7 @@ hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, cons
   p.lse = lse;
   p.lse2out = D + size_t(a.B) * a.H * a.N;
   const int64_t rows = int64_t(a.B) * a.H * a.N;
-  const int rpb = 256 / (a.d / 8);
+  const int rpb = 256 / 4;  // four lanes per row
   dim3 grid(unsigned((rows + rpb - 1) / rpb));
   if (a.d == 128) hipLaunchKernelGGL(bwd_dot_kernel<128>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(bwd_dot_kernel<64>, grid, dim3(256), 0, stream, p);
