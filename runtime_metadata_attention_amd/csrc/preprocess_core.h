@@ -152,30 +152,58 @@ __device__ __forceinline__ void wide_table_clear(const Role& r) {
   for (int t = threadIdx.x; t < total; t += kThreads) block[t] = make_uint2(0u, 0u);
 }
 
-// In-place inclusive prefix sums of a[0..T) and b[0..T) by one work-group.
+// In-place inclusive prefix sums of a[0..T) and b[0..T) by one work-group:
+// each thread sums a contiguous chunk, the chunk sums are scanned within each
+// wave by shuffles and across the waves through `part`, and each thread then
+// rewrites its chunk as running sums.  Two barriers.
 __device__ void scan2(int32_t* a, int32_t* b, int T, int32_t* part) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int chunk = (T + kThreads - 1) / kThreads;
   const int lo = t * chunk, hi = min(T, lo + chunk);
-  int32_t sa = 0, sb = 0;
-  for (int c = lo; c < hi; ++c) { sa += a[c]; sb += b[c]; }
-  part[t] = sa;
-  part[kThreads + t] = sb;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int32_t va = 0, vb = 0;
-    if (t >= off) { va = part[t - off]; vb = part[kThreads + t - off]; }
-    __syncthreads();
-    part[t] += va;
-    part[kThreads + t] += vb;
-    __syncthreads();
+  int32_t ca = 0, cb = 0;
+  for (int c = lo; c < hi; ++c) { ca += a[c]; cb += b[c]; }
+  int32_t sa = ca, sb = cb;  // inclusive scan of the chunk sums within the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t xa = __shfl_up(sa, off, 64), xb = __shfl_up(sb, off, 64);
+    if (lane >= off) { sa += xa; sb += xb; }
   }
-  int32_t ra = t > 0 ? part[t - 1] : 0, rb = t > 0 ? part[kThreads + t - 1] : 0;
+  if (lane == 63) { part[wv] = sa; part[kThreads + wv] = sb; }
+  __syncthreads();
+  int32_t ra = sa - ca, rb = sb - cb;  // exclusive: the chunks before this one
+  for (int w = 0; w < wv; ++w) { ra += part[w]; rb += part[kThreads + w]; }
   for (int c = lo; c < hi; ++c) {
     ra += a[c]; a[c] = ra;
     rb += b[c]; b[c] = rb;
   }
   __syncthreads();
+}
+
+// Bits 0..15 of x moved to the even bit positions 0, 2, .., 30.
+__device__ __forceinline__ uint32_t spread16(uint32_t x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  x = (x | (x << 1)) & 0x55555555u;
+  return x;
+}
+
+// Metadata checks of one padded sample (the CM_MD_* bits validate_sample
+// forms), spread over the work-group and OR-ed into *err.
+__device__ __forceinline__ void validate_sample_wg(int32_t N, int32_t n_seg, int32_t seg_cap, const int32_t* bounds,
+                                                   const int32_t* refs, int32_t n_refs, int32_t* err) {
+  const int t = threadIdx.x;
+  uint32_t e = 0;
+  if (n_seg < 0 || n_seg > seg_cap) {
+    e = t == 0 ? 1u : 0u;
+  } else if (n_seg >= 1) {
+    for (int i = t; i <= n_seg; i += kThreads) {
+      if (bounds[i] < 0 || bounds[i] > N) e |= 4u;
+      if (i < n_seg && bounds[i + 1] < bounds[i]) e |= 2u;
+    }
+    for (int i = t; i < n_seg * n_refs; i += kThreads)
+      if (refs[i] < -1 || refs[i] >= n_seg) e |= 8u;
+  }
+  if (e != 0) atomicOr(reinterpret_cast<uint32_t*>(err), e);
 }
 
 // The kernel body for one work-group; `prog` is the lowered program (both
@@ -239,8 +267,8 @@ __device__ __forceinline__ void preprocess_body(const PreprocessArgs& a, const i
                        (t < a.n_samples && a.cu_seqlens[t + 1] < c) || c < 0 || c > a.N;
       if (bad) atomicOr(reinterpret_cast<uint32_t*>(&L.misc[3]), kMdCuSeqlens);
     }
-  } else if (tid == 0) {
-    L.misc[1] = int32_t(validate_sample(a.N, n_seg, a.seg_cap, bounds, refs, a.n_refs));
+  } else {
+    validate_sample_wg(a.N, n_seg, a.seg_cap, bounds, refs, a.n_refs, &L.misc[1]);
   }
   __syncthreads();
   const uint32_t cu_err = uint32_t(L.misc[3]);
@@ -315,13 +343,19 @@ __device__ __forceinline__ void preprocess_body(const PreprocessArgs& a, const i
   __syncthreads();
   scan2(L.any, L.full, r.T, part);
 
-  for (int w = tid; w < r.W; w += kThreads) {
-    uint32_t word = 0;
-    for (int c = 16 * w; c < min(r.T, 16 * w + 16); ++c) {
-      const uint32_t code = L.any[c] == 0 ? 0u : (L.full[c] == r.nidx ? 1u : 2u);
-      word |= code << (2 * (c - 16 * w));
+  // tile codes (0 empty, 1 full, 2 partial), one tile per thread; each wave's
+  // 64 codes become four bitmap words from two ballots
+  for (int c0 = 0; c0 < r.T; c0 += kThreads) {
+    const int c = c0 + tid;
+    uint32_t code = 0;
+    if (c < r.T) code = L.any[c] == 0 ? 0u : (L.full[c] == r.nidx ? 1u : 2u);
+    const uint64_t lo = __ballot(int(code & 1u)), hi = __ballot(int(code >> 1));
+    const int lane = tid & 63;
+    const int w = (c0 + (tid & ~63)) / 16 + lane;
+    if (lane < 4 && w < r.W) {
+      const uint32_t l16 = uint32_t(lo >> (16 * lane)) & 0xFFFFu, h16 = uint32_t(hi >> (16 * lane)) & 0xFFFFu;
+      r.bitmap[w] = spread16(l16) | (spread16(h16) << 1);
     }
-    r.bitmap[w] = word;
   }
   if (tid == 0) {
     *r.tkmax = uint32_t(L.misc[0]);
