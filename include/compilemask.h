@@ -294,6 +294,24 @@ cm_status cm_attn_bwd(const cm_attn_args* args, const void* q, const void* k, co
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                       cm_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, allocation-free serving loops, harnesses that forbid hipMalloc):
+ * cm_attn_bwd with the workspace taken from a fixed array inside the library
+ * instead of a caller buffer.  The array holds D and the log2 lse of
+ * CM_NOALLOC_MAX_ROWS rows (16 MiB); every GPU the library runs on keeps its
+ * own copy until the process ends.  Its device address is looked up on the
+ * first call on each device; the call allocates and frees nothing.  Calls on
+ * one GPU share the array: two calls that overlap in time on the same GPU
+ * (other streams, other threads) race and give wrong results; calls in order
+ * on one stream are safe.  Every row the kernels read is written by the same
+ * call first, so nothing needs clearing.  CM_ERR_SIZE when B * H * N exceeds
+ * CM_NOALLOC_MAX_ROWS; otherwise the same arguments, checks, kernels and
+ * results as cm_attn_bwd. */
+#define CM_NOALLOC_MAX_ROWS (1 << 21)
+cm_status cm_attn_bwd_noalloc(const cm_attn_args* args, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dO, const cm_desc* desc,
+                              void* dq, void* dk, void* dv, cm_stream stream);
+
 /* One of the three backward kernels alone, same arguments as cm_attn_bwd
  * (stage 0: D, stage 1: dK/dV, stage 2: dQ), for per-kernel timing.  Running
  * stages 0, 1, 2 in order equals cm_attn_bwd. */

@@ -33,6 +33,7 @@ EXPORTS = ("cm_spec_compile", "cm_spec_free", "cm_spec_info", "cm_spec_dump", "c
            "cm_desc_size", "cm_desc_init", "cm_desc_size_packed", "cm_desc_init_packed", "cm_desc_free",
            "cm_desc_offsets", "cm_build_descriptor", "cm_build_blockmask",
            "cm_attn_fwd", "cm_attn_bwd_workspace", "cm_attn_bwd", "cm_attn_bwd_stage",
+           "cm_attn_bwd_noalloc",
            "cm_status_str", "cm_last_error", "cm_version")
 
 
@@ -100,6 +101,7 @@ def library() -> ctypes.CDLL:
         "cm_attn_bwd_workspace": (I32, [P(cm_attn_args), P(SZ)]),
         "cm_attn_bwd": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "cm_attn_bwd_stage": (I32, [I32, P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+        "cm_attn_bwd_noalloc": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]),
         "cm_status_str": (ctypes.c_char_p, [I32]),
         "cm_last_error": (ctypes.c_char_p, []),
         "cm_version": (ctypes.c_char_p, []),
@@ -367,6 +369,17 @@ def cm_attn_bwd_stage(stage: int, args: cm_attn_args, q, k, v, o, lse, do, desc,
     _check(library().cm_attn_bwd_stage(stage, ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        _ptr(do), _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                        _nbytes(workspace), _stream(stream)), "cm_attn_bwd_stage")
+
+
+CM_NOALLOC_MAX_ROWS = 1 << 21
+
+
+def cm_attn_bwd_noalloc(args: cm_attn_args, q, k, v, o, lse, do, desc, dq, dk, dv, stream=None):
+    """cm_attn_bwd with the library's fixed per-GPU workspace (no workspace
+    argument; at most CM_NOALLOC_MAX_ROWS rows B * H * N per call)."""
+    _check(library().cm_attn_bwd_noalloc(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                         _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "cm_attn_bwd_noalloc")
 
 
 def cm_status_str(status: int) -> str:

@@ -402,36 +402,60 @@ cm_status cm_attn_bwd_workspace(const cm_attn_args* args, size_t* bytes) {
   return CM_OK;
 }
 
-cm_status cm_attn_bwd_stage(int32_t stage, const cm_attn_args* args, const void* q, const void* k, const void* v,
-                            const void* o, const float* lse, const void* dO, const cm_desc* desc, void* dq, void* dk,
-                            void* dv, void* workspace, size_t workspace_bytes, cm_stream stream) {
+static cm_status bwd_run(int32_t stage, const cm_attn_args* args, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dO, const cm_desc* desc, void* dq, void* dk,
+                         void* dv, void* workspace, size_t workspace_bytes, bool fixed_scratch, cm_stream stream) {
   AttnDims dims;
   DescView view;
   cm_status st = check_attn(args, desc, dims, view);
   if (st != CM_OK) return st;
   if (stage < -1 || stage > 2) return fail(CM_ERR_INVALID, "stage must be 0, 1 or 2");
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
-    return fail(CM_ERR_NULL, "q, k, v, o, lse, dO, dq, dk, dv and workspace are required");
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || (!fixed_scratch && !workspace))
+    return fail(CM_ERR_NULL, fixed_scratch ? "q, k, v, o, lse, dO, dq, dk and dv are required"
+                                           : "q, k, v, o, lse, dO, dq, dk, dv and workspace are required");
   size_t need = 0;
   cm_attn_bwd_workspace(args, &need);
-  if (workspace_bytes < need) return fail(CM_ERR_SIZE, "workspace needs " + std::to_string(need) + " bytes");
+  if (fixed_scratch) {
+    const size_t rows = size_t(args->B) * args->H * args->N;
+    if (rows > kScratchRows)
+      return fail(CM_ERR_SIZE, "cm_attn_bwd_noalloc covers at most " + std::to_string(kScratchRows) +
+                                   " rows (B * H * N); this call has " + std::to_string(rows));
+  } else if (workspace_bytes < need) {
+    return fail(CM_ERR_SIZE, "workspace needs " + std::to_string(need) + " bytes");
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+      !aligned16(dk) || !aligned16(dv) || (!fixed_scratch && !aligned16(workspace)))
     return fail(CM_ERR_INVALID, "tensors must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* D = static_cast<float*>(workspace);
   hipError_t e = hipSuccess;
+  if (fixed_scratch) {
+    e = scratch_workspace(&D);
+    if (e != hipSuccess) return hip_fail(e, "cm_attn_bwd_noalloc (scratch address)");
+  }
   if (stage == -1 || stage == 0) e = launch_bwd_dot(dims, o, dO, lse, D, s);
   if (e == hipSuccess && (stage == -1 || stage == 1)) e = launch_bwd_dkdv(dims, q, k, v, lse, dO, D, view, dk, dv, s);
   if (e == hipSuccess && (stage == -1 || stage == 2)) e = launch_bwd_dq(dims, q, k, v, lse, dO, D, view, dq, s);
-  if (e != hipSuccess) return hip_fail(e, "cm_attn_bwd");
+  if (e != hipSuccess) return hip_fail(e, fixed_scratch ? "cm_attn_bwd_noalloc" : "cm_attn_bwd");
   return CM_OK;
+}
+
+cm_status cm_attn_bwd_stage(int32_t stage, const cm_attn_args* args, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dO, const cm_desc* desc, void* dq, void* dk,
+                            void* dv, void* workspace, size_t workspace_bytes, cm_stream stream) {
+  return bwd_run(stage, args, q, k, v, o, lse, dO, desc, dq, dk, dv, workspace, workspace_bytes, false, stream);
 }
 
 cm_status cm_attn_bwd(const cm_attn_args* args, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dO, const cm_desc* desc, void* dq, void* dk, void* dv, void* workspace,
                       size_t workspace_bytes, cm_stream stream) {
-  return cm_attn_bwd_stage(-1, args, q, k, v, o, lse, dO, desc, dq, dk, dv, workspace, workspace_bytes, stream);
+  return bwd_run(-1, args, q, k, v, o, lse, dO, desc, dq, dk, dv, workspace, workspace_bytes, false, stream);
+}
+
+cm_status cm_attn_bwd_noalloc(const cm_attn_args* args, const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dO, const cm_desc* desc, void* dq, void* dk, void* dv,
+                              cm_stream stream) {
+  return bwd_run(-1, args, q, k, v, o, lse, dO, desc, dq, dk, dv, nullptr, 0, true, stream);
 }
 
 const char* cm_status_str(cm_status status) {

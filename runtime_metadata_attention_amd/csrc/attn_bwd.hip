@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "attn_common.h"
 #include "internal.h"
@@ -597,6 +598,38 @@ BwdParams make_params(const AttnDims& a, const DescView& dv) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------ fixed scratch
+//
+// The backward's workspace (D and lse2 of every row) for callers that cannot
+// allocate: a file-scope device array of kScratchRows rows, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in; its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address reaches kernels.
+namespace {
+static __device__ __align__(256) float scratch[2 * kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_workspace(float** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, const float* lse, float* D,
                           hipStream_t stream) {

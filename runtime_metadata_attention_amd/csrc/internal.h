@@ -110,5 +110,10 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
 hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
                          const void* dO, const float* D, const DescView& dv, void* dq, hipStream_t stream);
 bool attn_tiles_supported(int d, int fq, int fk, int bk, int bq);
+// The fixed backward workspace of cm_attn_bwd_noalloc: 2 * kScratchRows floats
+// per GPU; *ptr = its device address on the current device (looked up once
+// per device).
+constexpr size_t kScratchRows = size_t(CM_NOALLOC_MAX_ROWS);
+hipError_t scratch_workspace(float** ptr);
 
 }  // namespace cm

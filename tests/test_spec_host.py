@@ -197,6 +197,12 @@ def test_argument_checks_without_gpu():
     args = cm.cm_attn_args(1 << 7, 1 << 4, 1 << 16, 128, 0, 0, 0, 0.0, 1)
     assert cm.library().cm_attn_fwd(args, None, 16, 16, None, 16, 16, None) == -1
     assert cm.cm_status_str(-4) == "descriptor/spec/argument mismatch"
+    # the fixed-workspace backward: more rows than its array holds is refused
+    # before any HIP call
+    big = cm.CM_NOALLOC_MAX_ROWS + 1
+    args = cm.cm_attn_args(1, 1, big, 128, 0, 0, 0, 0.0, 1)
+    assert cm.library().cm_attn_bwd_noalloc(args, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, None) == -6
+    assert "rows" in cm.cm_last_error()
 
 
 def test_specialised_source_embeds_the_program_and_compiles():
