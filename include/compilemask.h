@@ -132,8 +132,25 @@ typedef struct cm_attn_args {
   int64_t stride_b, stride_h, stride_n;
   float scale;
   int32_t causal;
-  int32_t check;   /* partial-tile visibility check, CM_CHECK_*; 0 = the default */
+  int32_t check;      /* partial-tile visibility check, CM_CHECK_*; 0 = the default */
+  int32_t precision;  /* P / dS operand precision, CM_PRECISION_*; 0 = the default */
 } cm_attn_args;
+
+/* Precision of the attention probabilities P and score gradients dS where
+ * they enter a matrix product (O = P V forward; dV = P^T dO, dK = dS^T Q,
+ * dQ = dS K backward).  The pages fix the result as plain masked softmax
+ * attention (paper summary, sections 2.1 and 3.3.2); the inputs are bf16 and
+ * every product accumulates in fp32.
+ *   CM_PRECISION_BF16 (the default): P and dS rounded once to bf16 (a
+ *     relative error of up to 2^-9 per element), as tiled attention kernels
+ *     usually do.
+ *   CM_PRECISION_SPLIT: P and dS enter as the sum of two bf16 values, hi =
+ *     bf16(x) and lo = bf16(x - hi) (about 2^-17 relative error), so every
+ *     product carries fp32 P and dS up to the order of accumulation; the
+ *     four products take two matrix instructions per operand pair.  Only
+ *     with CM_CHECK_RUN_BITS (else CM_ERR_UNSUPPORTED). */
+#define CM_PRECISION_BF16 0
+#define CM_PRECISION_SPLIT 1
 
 /* Partial-tile visibility checks (cm_attn_args.check).  All give identical
  * results; they differ only in the instructions the kernels spend on it.

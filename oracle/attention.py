@@ -87,10 +87,13 @@ def forward_head(q, k, v, mask_rows, b: int, rows=None, scale=None, block: int =
 
 
 def _rows_mask(mask_rows, b, rr):
+    """Mask rows rr (in the given order), one mask_rows call per run of
+    consecutive indices."""
     rr = np.asarray(rr)
     if len(rr) and np.all(np.diff(rr) == 1):
         return mask_rows(b, int(rr[0]), int(rr[-1]) + 1)
-    return np.vstack([mask_rows(b, int(r), int(r) + 1) for r in rr])
+    cuts = np.nonzero(np.diff(rr) != 1)[0] + 1
+    return np.vstack([mask_rows(b, int(g[0]), int(g[-1]) + 1) for g in np.split(rr, cuts)])
 
 
 def probabilities(q, k, lse, M, scale=None):
@@ -174,6 +177,55 @@ def backward(q, k, v, do, mask_rows, scale=None, block: int = 1024, stored_o=Non
             dq[b, h], dk[b, h], dv[b, h], O[b, h], lse[b, h] = backward_head(
                 q[b, h], k[b, h], v[b, h], do[b, h], mask_rows, b, scale=scale, block=block, stored_o=stored_o)
     return dq, dk, dv, O, lse
+
+
+def rows_seeing(mask_rows, b: int, N: int, keys, block: int = 2048) -> np.ndarray:
+    """Indices of the query rows of sample b that see at least one of `keys`."""
+    keys = np.asarray(keys)
+    out = []
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        hit = mask_rows(b, r0, r1)[:, keys].any(axis=1)
+        out.append(np.nonzero(hit)[0] + r0)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def tiles_head(q, k, v, do, mask_rows, b: int, rows, keys, scale=None, block: int = 1024, stored_o=None,
+               seeing=None):
+    """Exact outputs of one (b, h) pair at some query rows and some keys,
+    without the whole forward.
+
+    A key's dk and dv sum over the rows that see it (P is zero elsewhere), so
+    only those rows need their lse and D, which need only their own scores.
+    ``seeing`` may pass rows_seeing(mask_rows, b, N, keys) when the caller
+    already has it (it depends on the mask only, not on the head).  Returns
+    O, lse, dq at ``rows`` and dk, dv at ``keys`` (float64), as backward_head
+    would give them.
+    """
+    N, d = q.shape
+    sc = _scale(d, scale)
+    rows = np.asarray(rows)
+    keys = np.asarray(keys)
+    if seeing is None:
+        seeing = rows_seeing(mask_rows, b, N, keys)
+    need = np.union1d(rows, seeing)
+    O, lse = forward_head(q, k, v, mask_rows, b, rows=need, scale=scale, block=block)
+    Dvec = np.sum(do[need] * _o_for_d(O, stored_o), axis=1)
+    pos = np.searchsorted(need, rows)
+    M = _rows_mask(mask_rows, b, rows)
+    P = probabilities(q[rows], k, lse[pos], M, scale)
+    dS = P * (do[rows] @ v.T - Dvec[pos, None])
+    dq = (dS @ k) * sc
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    for a in range(0, len(need), block):
+        rr = need[a: a + block]
+        Mk = _rows_mask(mask_rows, b, rr)[:, keys]
+        Pk = probabilities(q[rr], k[keys], lse[a: a + len(rr)], Mk, scale)
+        dv += Pk.T @ do[rr]
+        dSk = Pk * (do[rr] @ v[keys].T - Dvec[a: a + len(rr), None])
+        dk += (dSk.T @ q[rr]) * sc
+    return dict(O=O[pos], lse=lse[pos], dq=dq, dk=dk, dv=dv)
 
 
 def sampled_head(q, k, v, do, mask_rows, b: int, rows, keys, scale=None, block: int = 1024, stored_o=None):

@@ -57,13 +57,17 @@ class cm_metadata(ctypes.Structure):
 class cm_attn_args(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
-                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("check", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("check", ctypes.c_int32),
+                ("precision", ctypes.c_int32)]
 
 
 CM_CHECK_RUN_BITS = 0
 CM_CHECK_ORDINARY_MASKED = 1
 CM_CHECK_PREDICATE = 2
 CM_CHECK_UNSIGNED = 3
+# P / dS operand precision (cm_attn_args.precision)
+CM_PRECISION_BF16 = 0
+CM_PRECISION_SPLIT = 1
 # predicate-baseline families (cm_build_blockmask)
 CM_PRED = {"causal": 0, "hstu": 1, "shared_prompt": 2, "retrieval": 3}
 
@@ -330,14 +334,16 @@ def cm_build_descriptor(spec: Spec, md: DeviceMetadata, desc: Descriptor, stream
 
 # ------------------------------------------------------------------ attention
 
-def attn_args(q, causal: bool = False, scale: float = 0.0, check: int = CM_CHECK_RUN_BITS) -> cm_attn_args:
+def attn_args(q, causal: bool = False, scale: float = 0.0, check: int = CM_CHECK_RUN_BITS,
+              precision: int = CM_PRECISION_BF16) -> cm_attn_args:
     """cm_attn_args from a [B, H, N, d] bf16 tensor's shape and strides; `check` selects the partial-tile
-    visibility check (CM_CHECK_UNSIGNED and CM_CHECK_ORDINARY_MASKED are the ablation kernels)."""
+    visibility check (CM_CHECK_UNSIGNED and CM_CHECK_ORDINARY_MASKED are the ablation kernels) and
+    `precision` the P / dS operand precision (CM_PRECISION_SPLIT: hi + lo bf16 pairs)."""
     B, H, N, d = q.shape
     sb, sh, sn, sd = q.stride()
     if sd != 1:
         raise ValueError("the last dimension must be contiguous")
-    return cm_attn_args(B, H, N, d, sb, sh, sn, float(scale), 1 if causal else 0, int(check))
+    return cm_attn_args(B, H, N, d, sb, sh, sn, float(scale), 1 if causal else 0, int(check), int(precision))
 
 
 def _desc_handle(desc):

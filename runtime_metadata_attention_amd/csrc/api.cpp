@@ -148,6 +148,11 @@ cm_status check_attn(const cm_attn_args* args, const cm_desc* desc, AttnDims& di
     return fail(CM_ERR_INVALID, "check must be CM_CHECK_RUN_BITS (0), CM_CHECK_ORDINARY_MASKED (1), CM_CHECK_PREDICATE (2) "
                                 "or CM_CHECK_UNSIGNED (3)");
   dims.check = args->check;
+  if (args->precision != CM_PRECISION_BF16 && args->precision != CM_PRECISION_SPLIT)
+    return fail(CM_ERR_INVALID, "precision must be CM_PRECISION_BF16 (0) or CM_PRECISION_SPLIT (1)");
+  if (args->precision == CM_PRECISION_SPLIT && args->check != CM_CHECK_RUN_BITS)
+    return fail(CM_ERR_UNSUPPORTED, "CM_PRECISION_SPLIT runs with the default check (CM_CHECK_RUN_BITS) only");
+  dims.precision = args->precision;
   if (args->check == CM_CHECK_PREDICATE && dims.causal)
     return fail(CM_ERR_INVALID, "the predicate baseline runs on a block-mask descriptor, not the maskless causal path");
   std::memset(&view, 0, sizeof(view));

@@ -112,8 +112,9 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ dK / dV
 
-template <int D, int BK, bool CAUSAL, int CHK>
+template <int D, int BK, bool CAUSAL, int CHK, int PREC>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr bool SPLIT = PREC == kPrecSplit;  // P and dS as hi + lo bf16 operand pairs
   constexpr int NW = BK / 32;
   static_assert(NW >= 2, "two waves copy lse2 and D");
   constexpr int TILE = BQ * D;                 // bf16 elements of one Q or dO tile
@@ -207,11 +208,19 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     const char* t = st + (i < NC ? TB : 0) + qc * (16 * D * 2);
     return lds_tr8_at(t + lo.tr(dbk, 0), t + lo.tr(dbk, 1));
   };
-  bf16x8 ppb[4], pdb[4];  // previous tile's P and dS (bf16); zero before the first tile
+  // previous tile's P and dS (bf16; with the split precision also their low
+  // parts); zero before the first tile
+  constexpr int NL = SPLIT ? 4 : 1;
+  bf16x8 ppb[4], pdb[4], ppl[NL], pdl[NL];
 #pragma unroll
   for (int qc = 0; qc < 4; ++qc) {
     ppb[qc] = as_bf16x8(make_uint4(0, 0, 0, 0));
     pdb[qc] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+#pragma unroll
+  for (int qc = 0; qc < NL; ++qc) {
+    ppl[qc] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    pdl[qc] = as_bf16x8(make_uint4(0, 0, 0, 0));
   }
   int pbuf = 0;
   const bool any_tile = have;
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
     // fenced chunks of four elements, each overlapped with 2NC/8 of the
     // previous tile's dV/dK MFMAs (operands read two MFMAs ahead, D one
     // chunk ahead).
-    bf16x8 pb[4], db8[4];
+    bf16x8 pb[4], db8[4], pl[NL], dl[NL];
     {
       constexpr int NM = 2 * NC, G = 2, MPC = NM / 8;
       const char* prv = lds0 + pbuf * (2 * TB);
@@ -319,6 +328,10 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
           const int j = i % NC, qc = j / (D / 32), dbk = j % (D / 32);
           if (i < NC) adv[dbk] = mfma32(op[i], ppb[qc], adv[dbk]);
           else adk[dbk] = mfma32(op[i], pdb[qc], adk[dbk]);
+          if constexpr (SPLIT) {
+            if (i < NC) adv[dbk] = mfma32(op[i], ppl[qc], adv[dbk]);
+            else adk[dbk] = mfma32(op[i], pdl[qc], adk[dbk]);
+          }
         }
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -329,22 +342,32 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
           const int qc = qb * 2 + (v >> 3), ee = v & 7;
           pb[qc][ee] = (__bf16)pe;
           db8[qc][ee] = (__bf16)ds;
+          if constexpr (SPLIT) {
+            pl[qc][ee] = bf16_lo(pe, pb[qc][ee]);
+            dl[qc][ee] = bf16_lo(ds, db8[qc][ee]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int qc = 0; qc < 4; ++qc) { ppb[qc] = pb[qc]; pdb[qc] = db8[qc]; }
+#pragma unroll
+    for (int qc = 0; qc < NL; ++qc) { ppl[qc] = pl[qc]; pdl[qc] = dl[qc]; }
     pbuf = buf;
     buf = buf == 2 ? 0 : buf + 1;
   }
   // the last tile's dV/dK (its stage is still intact: no copy was issued after it)
   if (any_tile) {
     const char* prv = lds0 + pbuf * (2 * TB);
-    mfma_stream<2 * NC, 4, 2>([&](int i) { return dvdk_read(prv, i); }, [&](int i, const bf16x8& a) {
+    mfma_stream<2 * NC, 4, 2, SPLIT ? 2 : 1>([&](int i) { return dvdk_read(prv, i); }, [&](int i, const bf16x8& a) {
       const int j = i % NC, qc = j / (D / 32), dbk = j % (D / 32);
       if (i < NC) adv[dbk] = mfma32(a, ppb[qc], adv[dbk]);
       else adk[dbk] = mfma32(a, pdb[qc], adk[dbk]);
+      if constexpr (SPLIT) {
+        if (i < NC) adv[dbk] = mfma32(a, ppl[qc], adv[dbk]);
+        else adk[dbk] = mfma32(a, pdl[qc], adk[dbk]);
+      }
     });
   }
 
@@ -370,8 +393,9 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ dQ
 
-template <int D, int BM, bool CAUSAL, int CHK>
+template <int D, int BM, bool CAUSAL, int CHK, int PREC>
 __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr bool SPLIT = PREC == kPrecSplit;  // dS as hi + lo bf16 operand pairs
   constexpr int NW = BM / 32;
   constexpr int TILE = BN * D;
   constexpr int TB = TILE * 2;
@@ -535,7 +559,7 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
         const char* t = cur + kc * (16 * D * 2);
         return lds_tr8_at(t + lo.tr(db, 0), t + lo.tr(db, 1));
       };
-      bf16x8 db8[4];
+      bf16x8 db8[4], dl8[SPLIT ? 4 : 1];
       bf16x8 op[NQ];
 #pragma unroll
       for (int kc = 0; kc <= 4; ++kc) {
@@ -549,12 +573,17 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
             const int i = (kc - 1) * MPK + m;
             if (i + G < NQ) op[i + G] = rd(i + G);
             acc[m] = mfma32(op[i], db8[kc - 1], acc[m]);
+            if constexpr (SPLIT) acc[m] = mfma32(op[i], dl8[kc - 1], acc[m]);
           }
         }
         if (kc < 4) {
           const int kb = kc >> 1, v0 = (kc & 1) * 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) db8[kc][e] = (__bf16)(s[kb][v0 + e] * (dp[kb][v0 + e] - Dq));
+          for (int e = 0; e < 8; ++e) {
+            const float ds = s[kb][v0 + e] * (dp[kb][v0 + e] - Dq);
+            db8[kc][e] = (__bf16)ds;
+            if constexpr (SPLIT) dl8[kc][e] = bf16_lo(ds, db8[kc][e]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -574,6 +603,43 @@ __global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
       }
     }
   }
+}
+
+// Kernel choice for one (head dim, tile) pair: the check and the causal
+// mode; the split precision exists for the default check only (the host
+// refuses other combinations).  Both kernels take 2 * tile lanes.
+struct DkdvLaunch {
+  template <int D, int T, bool C, int CHK, int PREC>
+  static void go(dim3 grid, const BwdParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, C, CHK, PREC>), grid, dim3(T * 2), 0, s, p);
+  }
+};
+struct DqLaunch {
+  template <int D, int T, bool C, int CHK, int PREC>
+  static void go(dim3 grid, const BwdParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, C, CHK, PREC>), grid, dim3(T * 2), 0, s, p);
+  }
+};
+
+template <class L, int D, int T>
+hipError_t dispatch(const AttnDims& a, dim3 grid, const BwdParams& p, hipStream_t s) {
+  const bool c = a.causal != 0;
+  if (a.precision == kPrecSplit) {
+    if (c) L::template go<D, T, true, kCheckRunBits, kPrecSplit>(grid, p, s);
+    else L::template go<D, T, false, kCheckRunBits, kPrecSplit>(grid, p, s);
+  } else if (a.check == kCheckPredicate) {
+    L::template go<D, T, false, kCheckPredicate, kPrecBf16>(grid, p, s);
+  } else if (a.check == kCheckOrdinaryMasked) {
+    if (c) L::template go<D, T, true, kCheckOrdinaryMasked, kPrecBf16>(grid, p, s);
+    else L::template go<D, T, false, kCheckOrdinaryMasked, kPrecBf16>(grid, p, s);
+  } else if (a.check == kCheckUnsigned) {
+    if (c) L::template go<D, T, true, kCheckUnsigned, kPrecBf16>(grid, p, s);
+    else L::template go<D, T, false, kCheckUnsigned, kPrecBf16>(grid, p, s);
+  } else {
+    if (c) L::template go<D, T, true, kCheckRunBits, kPrecBf16>(grid, p, s);
+    else L::template go<D, T, false, kCheckRunBits, kPrecBf16>(grid, p, s);
+  }
+  return hipGetLastError();
 }
 
 BwdParams make_params(const AttnDims& a, const DescView& dv) {
@@ -664,27 +730,9 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dvv);
   dim3 grid(p.Tk_b * a.H * a.B);
-  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate,
-             un = a.check == kCheckUnsigned;
-#define CM_DKDV(DD, BKK)                                                                                              \
-  do {                                                                                                               \
-    if (pr) {                                                                                                        \
-      hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckPredicate>), grid, dim3(BKK * 2), 0, stream, p);     \
-    } else if (o) {                                                                                                         \
-      if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckOrdinaryMasked>), grid, dim3(BKK * 2), 0, stream, p); \
-    } else if (un) { \
-      if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckUnsigned>), grid, dim3(BKK * 2), 0, stream, p); \
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckUnsigned>), grid, dim3(BKK * 2), 0, stream, p); \
-    } else { \
-      if (c) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, true, kCheckRunBits>), grid, dim3(BKK * 2), 0, stream, p); \
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, BKK, false, kCheckRunBits>), grid, dim3(BKK * 2), 0, stream, p); \
-    }                                                                                                                \
-  } while (0)
-  if (a.d == 128) { if (dv.bk == 128) CM_DKDV(128, 128); else CM_DKDV(128, 64); }
-  else { if (dv.bk == 128) CM_DKDV(64, 128); else CM_DKDV(64, 64); }
-#undef CM_DKDV
-  return hipGetLastError();
+  if (a.d == 128) return dv.bk == 128 ? dispatch<DkdvLaunch, 128, 128>(a, grid, p, stream)
+                                      : dispatch<DkdvLaunch, 128, 64>(a, grid, p, stream);
+  return dv.bk == 128 ? dispatch<DkdvLaunch, 64, 128>(a, grid, p, stream) : dispatch<DkdvLaunch, 64, 64>(a, grid, p, stream);
 }
 
 hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
@@ -699,27 +747,9 @@ hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const 
   p.lse2 = D + size_t(a.B) * a.H * a.N;
   p.dq = static_cast<uint16_t*>(dq);
   dim3 grid(p.Tq_f * a.H * a.B);
-  const bool c = a.causal != 0, o = a.check == kCheckOrdinaryMasked, pr = a.check == kCheckPredicate,
-             un = a.check == kCheckUnsigned;
-#define CM_DQ(DD, BMM)                                                                                              \
-  do {                                                                                                             \
-    if (pr) {                                                                                                      \
-      hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckPredicate>), grid, dim3(BMM * 2), 0, stream, p);     \
-    } else if (o) {                                                                                                       \
-      if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
-      else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckOrdinaryMasked>), grid, dim3(BMM * 2), 0, stream, p); \
-    } else if (un) { \
-      if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckUnsigned>), grid, dim3(BMM * 2), 0, stream, p); \
-      else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckUnsigned>), grid, dim3(BMM * 2), 0, stream, p); \
-    } else { \
-      if (c) hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, true, kCheckRunBits>), grid, dim3(BMM * 2), 0, stream, p); \
-      else hipLaunchKernelGGL((bwd_dq_kernel<DD, BMM, false, kCheckRunBits>), grid, dim3(BMM * 2), 0, stream, p); \
-    }                                                                                                              \
-  } while (0)
-  if (a.d == 128) { if (dv.fq == 128) CM_DQ(128, 128); else CM_DQ(128, 64); }
-  else { if (dv.fq == 128) CM_DQ(64, 128); else CM_DQ(64, 64); }
-#undef CM_DQ
-  return hipGetLastError();
+  if (a.d == 128) return dv.fq == 128 ? dispatch<DqLaunch, 128, 128>(a, grid, p, stream)
+                                      : dispatch<DqLaunch, 128, 64>(a, grid, p, stream);
+  return dv.fq == 128 ? dispatch<DqLaunch, 64, 128>(a, grid, p, stream) : dispatch<DqLaunch, 64, 64>(a, grid, p, stream);
 }
 
 }  // namespace cm

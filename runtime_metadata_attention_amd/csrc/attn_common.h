@@ -178,11 +178,12 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
 // A run of NM MFMAs whose A operands come from LDS: read(i) returns operand i
-// and mma(i, a) issues MFMA i.  Operand reads run G MFMAs ahead of their use
-// (a register pipeline of G + 1 operands), and the scheduling groups keep that
-// order: G reads, then (MFMA, next read) pairs.  RPO = LDS instructions per
-// operand (1 for ds_read_b128, 2 for a pair of transposed reads).
-template <int NM, int G, int RPO, class Read, class Mma>
+// and mma(i, a) issues MFMA i (MPO matrix instructions per operand).  Operand
+// reads run G MFMAs ahead of their use (a register pipeline of G + 1
+// operands), and the scheduling groups keep that order: G reads, then (MFMA,
+// next read) pairs.  RPO = LDS instructions per operand (1 for ds_read_b128,
+// 2 for a pair of transposed reads).
+template <int NM, int G, int RPO, int MPO = 1, class Read, class Mma>
 __device__ __forceinline__ void mfma_stream(Read&& read, Mma&& mma) {
   constexpr int G0 = G < NM ? G : NM;
   bf16x8 op[NM];
@@ -196,10 +197,22 @@ __device__ __forceinline__ void mfma_stream(Read&& read, Mma&& mma) {
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO * G0, 0);
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, MPO, 0);
     if (i + G < NM) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RPO, 0);
   }
 }
+
+// Precision of the probabilities (P) and score gradients (dS) where they
+// enter a matrix product as bf16 operands (PV forward; dV, dK, dQ backward).
+//   kPrecBf16 (the default): rounded to bf16 once, as tiled attention usually
+//     does: a relative error of up to 2^-9 per element.
+//   kPrecSplit: x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), two
+//     matrix instructions per operand pair, about 2^-17 relative error: the
+//     products then carry the fp32 values up to accumulation order.
+constexpr int kPrecBf16 = 0;
+constexpr int kPrecSplit = 1;
+
+__device__ __forceinline__ __bf16 bf16_lo(float x, __bf16 hi) { return (__bf16)(x - float(hi)); }
 
 // Offset, inside a 64-wide tile, of element v of 32-block blk of a score
 // tile in C layout, for the lane half h = 0 (add 4h for the other half).

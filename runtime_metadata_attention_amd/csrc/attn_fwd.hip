@@ -46,7 +46,7 @@ struct FwdParams {
 constexpr int BN = 64;
 constexpr int MAXR = 4;  // runs kept in registers; more are read from memory
 
-template <int D, int BM, bool CAUSAL, int CHK>
+template <int D, int BM, bool CAUSAL, int CHK, int PREC>
 __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int NW = BM / 32;
   // K and V tiles, double-buffered, swizzled (see swz())
@@ -177,7 +177,8 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     }
     const float mu = (m == -INFINITY) ? 0.f : m;
     float rsum = 0.f;
-    bf16x8 pb[4];
+    constexpr bool SPLIT = PREC == kPrecSplit;
+    bf16x8 pb[4], pl[SPLIT ? 4 : 1];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -185,18 +186,23 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][(kc & 1) * 8 + e], p.scale_log2, -mu));
         rsum += pe;
         pb[kc][e] = (__bf16)pe;
+        if constexpr (SPLIT) pl[kc][e] = bf16_lo(pe, pb[kc][e]);
       }
     }
     lsum += rsum;
 
-    // O^T += V^T P^T (V read transposed from LDS)
-    mfma_stream<4 * (D / 32), 4, 2>(
+    // O^T += V^T P^T (V read transposed from LDS; with the split precision
+    // each V operand multiplies P's high and low bf16 parts)
+    mfma_stream<4 * (D / 32), 4, 2, SPLIT ? 2 : 1>(
         [&](int i) {
           const int kc = i / (D / 32), db = i % (D / 32);
           const char* t = cV + kc * (16 * D * 2);
           return lds_tr8_at(t + lo.tr(db, 0), t + lo.tr(db, 1));
         },
-        [&](int i, const bf16x8& a) { acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]); });
+        [&](int i, const bf16x8& a) {
+          acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]);
+          if constexpr (SPLIT) acc[i % (D / 32)] = mfma32(a, pl[i / (D / 32)], acc[i % (D / 32)]);
+        });
   }
 
   // epilogue: O = acc / l, lse = ln-sum-exp (natural log)
@@ -221,15 +227,20 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BM, bool CAUSAL, int CHK>
+template <int D, int BM, bool CAUSAL, int CHK, int PREC = kPrecBf16>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   dim3 grid(p.Tq * p.H * p.B);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BM, CAUSAL, CHK>), grid, dim3(BM * 2), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BM, CAUSAL, CHK, PREC>), grid, dim3(BM * 2), 0, stream, p);
   return hipGetLastError();
 }
 
+// (the split precision exists for the default check only: the host refuses
+// other combinations)
 template <int D, int BM>
-hipError_t launch_dc(const FwdParams& p, bool causal, int check, hipStream_t stream) {
+hipError_t launch_dc(const FwdParams& p, bool causal, int check, int prec, hipStream_t stream) {
+  if (prec == kPrecSplit)
+    return causal ? launch<D, BM, true, kCheckRunBits, kPrecSplit>(p, stream)
+                  : launch<D, BM, false, kCheckRunBits, kPrecSplit>(p, stream);
   if (check == kCheckPredicate) return launch<D, BM, false, kCheckPredicate>(p, stream);
   if (check == kCheckOrdinaryMasked)
     return causal ? launch<D, BM, true, kCheckOrdinaryMasked>(p, stream) : launch<D, BM, false, kCheckOrdinaryMasked>(p, stream);
@@ -264,8 +275,10 @@ hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, cons
   p.pred.n_scalars = dv.pred.n_scalars; p.pred.refs = dv.pred.refs; p.pred.seg_cap = dv.pred.seg_cap;
   p.pred.n_refs = dv.pred.n_refs; p.pred.sample_err = dv.pred.sample_err;
   const bool c = a.causal != 0;
-  if (a.d == 128) return dv.fq == 128 ? launch_dc<128, 128>(p, c, a.check, stream) : launch_dc<128, 64>(p, c, a.check, stream);
-  return dv.fq == 128 ? launch_dc<64, 128>(p, c, a.check, stream) : launch_dc<64, 64>(p, c, a.check, stream);
+  const int pr = a.precision;
+  if (a.d == 128)
+    return dv.fq == 128 ? launch_dc<128, 128>(p, c, a.check, pr, stream) : launch_dc<128, 64>(p, c, a.check, pr, stream);
+  return dv.fq == 128 ? launch_dc<64, 128>(p, c, a.check, pr, stream) : launch_dc<64, 64>(p, c, a.check, pr, stream);
 }
 
 }  // namespace cm

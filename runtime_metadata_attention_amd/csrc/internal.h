@@ -75,8 +75,8 @@ struct AttnDims {
   int64_t sb, sh, sn;            // element strides of the bf16 tensors
   float scale;
   int32_t causal;
-  int32_t check;                 // partial-tile check: 0 unsigned visible runs, 1 ordinary masked
-                                 // intervals, 2 the predicate baseline
+  int32_t check;                 // partial-tile check, CM_CHECK_*
+  int32_t precision;             // P / dS operand precision, CM_PRECISION_*
 };
 struct PredView {                // predicate-baseline inputs (block-mask descriptors)
   int32_t family;                 // -1: an interval descriptor

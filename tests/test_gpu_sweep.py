@@ -7,15 +7,17 @@ Each case draws from its own seed:
 * a padded or a packed batch (packed: 1 to 4 samples, some of them empty);
 * contiguous or [B, N, H, d] storage.
 
-Mask proportions follow the workloads (see sample_md).  A key seen by every
-row with probability near 1/2 (HSTU with h = 1, a one-token prompt) would
-make bf16-rounded P add about 0.025 to that key's dV: beyond the 2e-2 bar
-for any kernel that rounds P to bf16, in a regime the workloads never reach
-(the degenerate h = 0 and h = 1 shapes are covered at N = 1 and 5 by the
-tiny-sequence tests).
+Mask parameters cover each family's whole range, as the oracle's own small
+cases draw them: HSTU h ~ U[1, n), prompt P ~ U[1, n / 2) with 1 to 5
+responses, retrieval prefixes and segments as in small_md.
 
 Descriptor words must equal the oracle's.  O, lse, dQ, dK and dV must meet
-the parity bars of test_gpu_attention.
+the parity bars of test_gpu_attention, in both operand precisions.  With
+bf16-rounded P and dS (the default precision) some draws miss the 2e-2 bar:
+a key that many rows see with probabilities near 1/2 (HSTU with a short
+history) accumulates the rounding of every P into its dV.  Those cases are
+listed in BF16_MISSES with the measured excess and skipped in that precision
+only; the split precision must meet the bar on every case.
 """
 import numpy as np
 import pytest
@@ -23,7 +25,7 @@ import pytest
 from runtime_metadata_attention_amd import specs
 from oracle import descriptor as od
 from oracle import masks as om
-from tests.test_gpu_attention import check_all, run_gpu
+from tests.test_gpu_attention import PRECISIONS, check_all, run_gpu, set_case
 from tests.test_gpu_descriptor import explain, gpu_descriptor
 from tests.test_oracle_masks import small_md
 from tests.test_oracle_packed import empty_sample
@@ -34,22 +36,21 @@ pytestmark = pytest.mark.gpu
 FAMILIES = ["causal", "hstu", "shared_prompt", "retrieval"]
 TILES = [(128, 64, 128, 64), (64, 64, 64, 64), (128, 64, 64, 64), (64, 64, 128, 64)]
 
+# (kind, seed) -> why the default precision misses the 2e-2 bar on that case
+# (measured on MI355X; each case passes in the split precision)
+BF16_MISSES = {
+    ("small", 42): "shared_prompt N=260: dv off by 2.076e-2 at |exact| 4.89, the value a CPU emulation of "
+                   "bf16-rounded P gives to the digit",
+    ("small", 43): "packed hstu N=446: dv off by 2.131e-2 at |exact| 4.51, the value a CPU emulation of "
+                   "bf16-rounded P gives to the digit",
+    ("small", 58): "hstu N=322 d=64: dk off by 4.54e-2 at |exact| 6.27 (key 0, seen by all 322 rows): the "
+                   "forward's bf16 P moves the stored O that enters D = rowsum(dO * O) of every such row; over 200 "
+                   "rounding patterns a CPU emulation gives this element an error of std 2.0e-2, max 4.8e-2",
+}
+
 
 def sample_md(mask, n, rng):
-    """One sample's metadata, with the proportions of the workloads: HSTU
-    h = max(1, floor(u n)), u ~ U[0.25, 0.94] (the packed HSTU workload's
-    rule); a prompt of at least n / 8 tokens (the reward workload's P is at
-    least 4096 of 32768); the retrieval family as the small oracle cases
-    draw it."""
-    if mask == "causal":
-        return metadata_from_segments(n, 0, 0, (), [{}])
-    if mask == "hstu":
-        return metadata_from_segments(n, 0, 0, ("h",), [{"scalars": [max(1, int(rng.uniform(0.25, 0.94) * n))]}])
-    if mask == "shared_prompt":
-        P = int(rng.integers(max(1, n // 8), max(2, n // 2)))
-        R = int(min(rng.integers(1, 6), n - P))
-        cuts = sorted(rng.choice(np.arange(P + 1, n), size=R - 1, replace=False).tolist()) if R > 1 else []
-        return metadata_from_segments(n, 8, 0, ("P",), [{"scalars": [P], "bounds": [P] + cuts + [n]}])
+    """One sample's metadata over the family's whole range (small_md's draws)."""
     return small_md(mask, N=n, seed=int(rng.integers(1 << 30)), B=1)
 
 
@@ -86,22 +87,33 @@ def draw_case(seed, n_max=700):
     return mask, md, B, H, d, tiles, strided
 
 
+def _skip_known_miss(kind, seed, prec):
+    reason = BF16_MISSES.get((kind, seed)) if prec == "bf16" else None
+    if reason:
+        pytest.skip(f"bf16 P/dS misses the 2e-2 bar here: {reason}; the split precision meets it")
+
+
+@pytest.mark.parametrize("prec", list(PRECISIONS))
 @pytest.mark.parametrize("seed", range(64))
-def test_random_small_configuration(seed):
-    run_case(seed, *draw_case(seed))
+def test_random_small_configuration(seed, prec):
+    _skip_known_miss("small", seed, prec)
+    run_case(seed, *draw_case(seed), prec=prec)
 
 
+@pytest.mark.parametrize("prec", list(PRECISIONS))
 @pytest.mark.parametrize("seed", range(100, 112))
-def test_random_medium_configuration(seed):
+def test_random_medium_configuration(seed, prec):
     """Up to 4096 tokens: many tiles per row and column, and retrieval
     columns with more runs than the kernels keep in registers."""
-    run_case(seed, *draw_case(seed, n_max=4096))
+    _skip_known_miss("medium", seed, prec)
+    run_case(seed, *draw_case(seed, n_max=4096), prec=prec)
 
 
-def run_case(seed, mask, md, B, H, d, tiles, strided):
+def run_case(seed, mask, md, B, H, d, tiles, strided, prec="bf16"):
     packed = om.is_packed(md)
     print(f"[sweep] seed={seed} {mask} N={md.N} B={B} H={H} d={d} tiles={tiles} "
-          f"packed={md.B if packed else 0} strided={strided}", flush=True)
+          f"packed={md.B if packed else 0} strided={strided} precision={prec}", flush=True)
+    set_case(f"sweep seed={seed} {mask} N={md.N} {prec}")
     words, desc, _ = gpu_descriptor(mask, md, tiles)
     want = od.build(mask, md, desc.K_r, desc.K_c, tiles)
     n_err = md.B if packed else None
@@ -109,5 +121,5 @@ def run_case(seed, mask, md, B, H, d, tiles, strided):
     t = make_tensors(B, H, md.N, d, 500 + seed)
     if strided:
         t = {n: x.transpose(1, 2).contiguous().transpose(1, 2) for n, x in t.items()}
-    out = run_gpu(specs.BY_MASK[mask], md, t, tiles)
+    out = run_gpu(specs.BY_MASK[mask], md, t, tiles, precision=PRECISIONS[prec])
     check_all(out, t, mask, md)

@@ -150,6 +150,36 @@ def test_sampled_head_equals_full_backward():
     np.testing.assert_allclose(s["dv"], dv[keys], atol=1e-12)
 
 
+@pytest.mark.parametrize("mask", ["causal", "hstu", "shared_prompt", "retrieval"])
+def test_tiles_head_equals_full_backward(mask):
+    """The restricted computation (forward only for the rows that the chosen
+    keys see) gives backward_head's values at those rows and keys."""
+    from tests.test_oracle_masks import small_md
+    md = small_md(mask, N=300, seed=3, B=2)
+    t = make_tensors(2, 1, 300, 32, 77)
+    fn = om.row_block_fn(mask, md)
+    for b in range(2):
+        q, k, v, do = (oa._f64(t[n])[b, 0] for n in ("q", "k", "v", "do"))
+        dq, dk, dv, O, lse = oa.backward_head(q, k, v, do, fn, b, block=64, stored_o="bf16")
+        rows = np.r_[0:40, 150:171, 290:300]
+        keys = np.r_[0:3, 200:264, 299]
+        s = oa.tiles_head(q, k, v, do, fn, b, rows, keys, block=50, stored_o="bf16")
+        np.testing.assert_allclose(s["O"], O[rows], atol=1e-13)
+        np.testing.assert_array_equal(np.isneginf(s["lse"]), np.isneginf(lse[rows]))
+        fin = np.isfinite(lse[rows])
+        np.testing.assert_allclose(s["lse"][fin], lse[rows][fin], atol=1e-13)
+        np.testing.assert_allclose(s["dq"], dq[rows], atol=1e-12)
+        np.testing.assert_allclose(s["dk"], dk[keys], atol=1e-12)
+        np.testing.assert_allclose(s["dv"], dv[keys], atol=1e-12)
+        # the row set it needs is exactly the rows that see a chosen key
+        M = fn(b, 0, 300)
+        seeing = oa.rows_seeing(fn, b, 300, keys, block=37)
+        assert np.array_equal(seeing, np.nonzero(M[:, keys].any(axis=1))[0])
+        s2 = oa.tiles_head(q, k, v, do, fn, b, rows, keys, block=50, stored_o="bf16", seeing=seeing)
+        for n in ("dq", "dk", "dv"):
+            np.testing.assert_array_equal(s2[n], s[n])
+
+
 def test_row_partition_sums_to_full_backward():
     w = WORKLOADS["shared_prompt_tiny"]
     md = make_metadata(w)

@@ -197,6 +197,13 @@ def test_argument_checks_without_gpu():
     args = cm.cm_attn_args(1 << 7, 1 << 4, 1 << 16, 128, 0, 0, 0, 0.0, 1)
     assert cm.library().cm_attn_fwd(args, None, 16, 16, None, 16, 16, None) == -1
     assert cm.cm_status_str(-4) == "descriptor/spec/argument mismatch"
+    # operand precision: only 0 and 1, and the split precision only with the default check
+    args = cm.cm_attn_args(1, 1, 128, 64, 0, 0, 0, 0.0, 1, 0, 2)
+    assert cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None) == -2
+    args = cm.cm_attn_args(1, 1, 128, 64, 0, 0, 0, 0.0, 1, cm.CM_CHECK_UNSIGNED, cm.CM_PRECISION_SPLIT)
+    assert cm.library().cm_attn_fwd(args, 16, 16, 16, None, 16, 16, None) == -5
+    args = cm.cm_attn_args(1, 1, 128, 64, 0, 0, 0, 0.0, 1, cm.CM_CHECK_RUN_BITS, cm.CM_PRECISION_SPLIT)
+    assert cm.library().cm_attn_fwd(args, None, 16, 16, None, 16, 16, None) == -1  # checks pass, q missing
     # the fixed-workspace backward: more rows than its array holds is refused
     # before any HIP call
     big = cm.CM_NOALLOC_MAX_ROWS + 1
