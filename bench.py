@@ -7,9 +7,17 @@ forward + backward, 14 * d * V / step time, where V is the exact number of
 visible (query, key) pairs of the batch summed over heads (4 d V forward,
 10 d V backward); the preprocess time is inside the step and reported alone.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision bf16|split]
 
-Prints one JSON line on stdout.  Progress goes to stderr.
+Prints one JSON line on stdout.  Progress goes to stderr.  Besides the
+default workload (reward_model_32k) the line carries `by_workload`: the other
+32K workload (retrieval4_32k) and the causal check (causal_8k through the
+descriptor and through the maskless causal path, and their ratio), measured
+the same way in the same run.
+
+Step times come from HIP events around every kernel of every timed step;
+`ms_per_step` is the wall clock over the timed steps, `step_ms` the median
+and 10th/90th percentiles of the per-step event times.
 
 HBM traffic of the dominant kernel comes from rocprofv3 counter runs:
 
@@ -21,6 +29,15 @@ HBM traffic of the dominant kernel comes from rocprofv3 counter runs:
 
 The copy runs time a plain device-to-device copy of known size; the ratio of
 its true bytes to what the counters report scales the kernel's counts.
+
+The clock of each kernel comes from a GRBM_GUI_ACTIVE counter run (GPU busy
+cycles, summed over the 8 XCDs) over each dispatch's duration:
+
+    rocprofv3 --pmc GRBM_GUI_ACTIVE -f csv -d OUT/clock -o run -- python bench.py --steps 20 --warmup 1 --no-cpu-baseline --no-extra
+    python bench.py --record-clock OUT/clock
+
+and the roofline then also reports the fraction of the peak at that clock
+(256 CUs x 4096 bf16 flop per CU and cycle x f).
 """
 from __future__ import annotations
 
@@ -38,6 +55,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+BF16_FLOP_PER_CLK = 256 * 4096  # MI355X: 256 CUs x 4096 dense bf16 flop per CU and cycle
+EXTRA_WORKLOADS = (("retrieval4_32k", False), ("causal_8k", False), ("causal_8k", True))
 KERNEL_SOURCES = {
     "attn_fwd_kernel": "attn_fwd.hip",
     "bwd_dkdv_kernel": "attn_bwd.hip",
@@ -68,6 +87,68 @@ def traffic_for(kernel: str, workload: str):
     if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def clock_for(kernel: str, workload: str):
+    """Mean clock (GHz) of the kernel over its dispatches in a GRBM_GUI_ACTIVE
+    counter run (profiles/clock.json), or None when no measurement matches the
+    kernel's current source."""
+    p = os.path.join(ROOT, "profiles", "clock.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("clock_ghz_mean")
+
+
+def record_clock(csv_dir: str, workload: str = "reward_model_32k"):
+    """Per dispatch: GRBM_GUI_ACTIVE / 8 XCDs = the kernel's cycles; over its
+    duration in the counter run = its average clock.  Writes profiles/clock.json
+    and prints a markdown summary with every dispatch (duration and clock)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != "GRBM_GUI_ACTIVE":
+                continue
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            d = per.setdefault(key, {"cycles": 0.0, "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d["cycles"] += float(r["Counter_Value"])
+    path = os.path.join(ROOT, "profiles", "clock.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    lines = ["| kernel | dispatch | duration us | cycles (GRBM_GUI_ACTIVE / 8) | clock GHz |", "|---|---|---|---|---|"]
+    for kernel in KERNEL_SOURCES:
+        rows = sorted((k[1], v) for k, v in per.items() if kernel in k[0])
+        if not rows:
+            continue
+        clocks = []
+        for disp, v in rows:
+            cyc = v["cycles"] / 8.0
+            ghz = cyc / v["ns"] if v["ns"] > 0 else float("nan")
+            clocks.append(ghz)
+            lines.append(f"| `{kernel}` | {disp} | {v['ns'] / 1e3:.1f} | {cyc:.4g} | {ghz:.3f} |")
+        rec[f"{kernel}@{workload}"] = {"source_hash": source_hash(kernel), "clock_ghz_mean": round(float(np.mean(clocks)), 4),
+                                       "clock_ghz_min": round(float(np.min(clocks)), 4),
+                                       "clock_ghz_max": round(float(np.max(clocks)), 4), "dispatches": len(clocks),
+                                       "duration_us": [round(v["ns"] / 1e3, 1) for _, v in rows],
+                                       "clock_ghz": [round(c, 4) for c in clocks]}
+    json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 COPY_BYTES = 1 << 30
@@ -162,23 +243,24 @@ def cpu_baseline(name: str, budget_s: float = 20.0):
     t = make_tensors(1, 1, w.N, w.d, w.seed)
     q, k, v, do = (oa._f64(t[n])[0, 0] for n in ("q", "k", "v", "do"))
     fn = om.row_block_fn(w.mask, md)
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    cores = len(os.sched_getaffinity(0))
     rows, spent, vis = 64, 0.0, 0
-    while True:
-        r1 = w.N
-        r0 = max(0, r1 - rows)
-        t0 = time.perf_counter()
-        oa.backward_rows(q, k, v, do, fn, 0, r0, r1)
-        spent = time.perf_counter() - t0
-        vis = int(fn(0, r0, r1).sum())
-        if spent > budget_s / 4 or r0 == 0:
-            break
-        rows *= 4
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        while True:
+            r1 = w.N
+            r0 = max(0, r1 - rows)
+            t0 = time.perf_counter()
+            oa.backward_rows(q, k, v, do, fn, 0, r0, r1)
+            spent = time.perf_counter() - t0
+            vis = int(fn(0, r0, r1).sum())
+            if spent > budget_s / 4 or r0 == 0:
+                break
+            rows *= 4
     tflops = 14.0 * w.d * vis / spent / 1e12
-    return {"value": tflops, "unit": "visible-pair TFLOP/s (fp64 oracle)", "cores": threads, "kind": "oracle",
+    return {"value": tflops, "unit": "visible-pair TFLOP/s (fp64 oracle)", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{name}: sample 0, head 0, query rows {r0}..{r1 - 1} ({vis} visible pairs), forward + "
-                      f"backward, {spent:.2f} s", "seconds": spent}
+                      f"backward, {spent:.2f} s with BLAS on {cores} threads", "seconds": spent}
 
 
 def main():
@@ -188,6 +270,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="reward_model_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="leave out the by_workload measurements")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "split"],
+                    help="P / dS operand precision (split: hi + lo bf16 pairs)")
+    ap.add_argument("--split-cost", action="store_true",
+                    help="also time every workload in both operand precisions (JSON lines to stderr)")
     ap.add_argument("--causal-path", action="store_true", help="time the maskless causal path (causal masks only)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload (and the causal comparator) and write one JSON line per run "
@@ -206,9 +293,13 @@ def main():
                     help="also time every workload's step eagerly and as a HIP graph replay; JSON lines to stderr")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the plain copy for counter scaling")
     ap.add_argument("--record-traffic", metavar="DIR", help="write profiles/traffic.json from counter runs in DIR")
+    ap.add_argument("--record-clock", metavar="DIR", help="write profiles/clock.json from a GRBM_GUI_ACTIVE run in DIR")
     a = ap.parse_args()
     if a.record_traffic:
         record_traffic(a.record_traffic, a.workload)
+        return
+    if a.record_clock:
+        record_clock(a.record_clock, a.workload)
         return
     if a.copy_calibration:
         copy_calibration()
@@ -260,7 +351,30 @@ def main():
                    "descriptor_build_us": base["preprocess_us"], "blockmask_build_us": pred["preprocess_us"],
                    "descriptor_kernel_ms": base["kernel_ms"], "predicate_kernel_ms": pred["kernel_ms"]}
             print("[bench-predicate] " + json.dumps(rec), file=sys.stderr, flush=True)
-    line = measure(a.workload, a.causal_path, a.steps, a.warmup, cpu=not a.no_cpu_baseline)
+    if a.split_cost:
+        for name in WORKLOADS:
+            base = measure(name, False, a.steps, a.warmup, cpu=False)
+            spl = measure(name, False, a.steps, a.warmup, cpu=False, precision="split")
+            rec = {"workload": name, "bf16_ms": base["step_ms"]["median"], "split_ms": spl["step_ms"]["median"],
+                   "cost": round(spl["step_ms"]["median"] / base["step_ms"]["median"] - 1.0, 4),
+                   "bf16_kernel_ms": base["kernel_ms"], "split_kernel_ms": spl["kernel_ms"]}
+            print("[bench-split] " + json.dumps(rec), file=sys.stderr, flush=True)
+    prec = a.precision
+    line = measure(a.workload, a.causal_path, a.steps, a.warmup, cpu=not a.no_cpu_baseline, precision=prec)
+    if not a.no_extra:
+        extra = {}
+        for name, causal in EXTRA_WORKLOADS:
+            if name == a.workload and causal == a.causal_path:
+                continue
+            m = measure(name, causal, a.steps, a.warmup, cpu=False, precision=prec)
+            extra[name + ("_maskless_causal" if causal else "")] = {
+                k: m[k] for k in ("value", "frac_peak", "ms_per_step", "step_ms", "preprocess_us", "fwd_tflops",
+                                  "bwd_tflops", "kernel_ms")} | {"visible_pairs": m["config"]["visible_pairs"],
+                                                                 "roofline": m["roofline"]}
+        if "causal_8k" in extra and "causal_8k_maskless_causal" in extra:
+            extra["causal_8k_descriptor_vs_maskless"] = round(
+                extra["causal_8k_maskless_causal"]["step_ms"]["median"] / extra["causal_8k"]["step_ms"]["median"], 4)
+        line["by_workload"] = extra
     print(json.dumps(line), flush=True)
 
 
@@ -355,7 +469,7 @@ def time_graph(name: str, steps: int, warmup: int) -> dict:
 
 
 def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool, check: int = 0,
-            predicate: bool = False) -> dict:
+            predicate: bool = False, precision: str = "bf16") -> dict:
     """One bench line.  predicate=True times the predicate baseline: the block
     mask rebuilt from the metadata every step (cm_build_blockmask) and the
     predicate evaluated in partial tiles (check CM_CHECK_PREDICATE)."""
@@ -378,7 +492,8 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
     dmd = cm.device_metadata(md, dev)
     if predicate:
         check = cm.CM_CHECK_PREDICATE
-    args = cm.attn_args(q, causal=causal_path, check=check)
+    prec = {"bf16": cm.CM_PRECISION_BF16, "split": cm.CM_PRECISION_SPLIT}[precision]
+    args = cm.attn_args(q, causal=causal_path, check=check, precision=prec)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -423,6 +538,9 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
             per[i, j] = e[j].elapsed_time(e[j + 1])  # ms
     avg = per.mean(axis=0)
     ms_step = wall * 1e3 / steps
+    step_ev = np.array([e[0].elapsed_time(e[5]) for e in evs])  # ms, first to last event of each step
+    step_ms = {"median": round(float(np.median(step_ev)), 4), "p10": round(float(np.percentile(step_ev, 10)), 4),
+               "p90": round(float(np.percentile(step_ev, 90)), 4)}
     log("per-kernel ms: " + ", ".join(f"{n}={x:.4f}" for n, x in zip(names, avg)))
 
     d = w.d
@@ -434,7 +552,8 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
     times = dict(zip(names, avg))
     dom = max(alg, key=lambda n: times[n])
     achieved = alg[dom] / (times[dom] * 1e-3) / 1e12
-    traffic = traffic_for(dom, w.name)
+    traffic = traffic_for(dom, w.name) if precision == "bf16" and check == 0 and not causal_path else None
+    clock = clock_for(dom, w.name) if precision == "bf16" and check == 0 and not causal_path else None
     pre_bytes = desc.bytes + sum(x.numel() * 4 for x in (dmd.scalars, dmd.seg_bounds, dmd.n_seg, dmd.refs)
                                  if x is not None)
     line = {
@@ -445,6 +564,7 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -453,7 +573,8 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tiles": list(w.tiles),
                    "seed": w.seed, "visible_pairs": V, "path": "causal" if causal_path else "descriptor",
                    "packed_samples": int(md.B) if w.packed else 0,
-                   "check": {0: "run_bits", 1: "ordinary_masked", 2: "predicate", 3: "unsigned"}[check]},
+                   "check": {0: "run_bits", 1: "ordinary_masked", 2: "predicate", 3: "unsigned"}[check],
+                   "precision": precision},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "preprocess_us": round(times["preprocess_kernel"] * 1e3, 2),
         "preprocess_GBps": round(pre_bytes / (times["preprocess_kernel"] * 1e-3) / 1e9, 1),
@@ -462,7 +583,11 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
                                              times["bwd_dq_kernel"]) * 1e-3) / 1e12, 2),
         "kernel_ms": {n: round(float(x), 4) for n, x in times.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "clock_GHz": clock,
+                     "peak_at_clock": None if clock is None else round(BF16_FLOP_PER_CLK * clock * 1e9 / 1e12, 1),
+                     "frac_at_clock": None if clock is None else
+                     round(achieved / (BF16_FLOP_PER_CLK * clock * 1e9 / 1e12), 4)},
     }
     if cpu:
         log("timing the CPU oracle on a bounded sample")

@@ -209,13 +209,21 @@ cm_status cm_spec_eval_host(const cm_spec* spec, int32_t direction, int32_t N, i
 
 /* ---- descriptor memory (caller-owned) ---------------------------------- */
 
-/* Bytes of a descriptor for (spec, B, N, seg_cap, tiles). */
+/* Bytes of a descriptor for (spec, B, N, seg_cap, tiles): the Execution
+ * Descriptor of paper summary section 3.3.1 (interval tables padded to the
+ * spec's slot counts, two-bit tile states per direction) in the layout at the
+ * top of this header.  Host only; CM_ERR_INVALID for sizes out of range. */
 cm_status cm_desc_size(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap,
                        const cm_tiles* tiles, size_t* bytes);
 
 /* Bind a caller-owned device buffer of at least cm_desc_size() bytes to a new
  * descriptor handle and zero it (synchronously, once).  The handle does not
- * own dev_buf; free the handle with cm_desc_free and the buffer yourself. */
+ * own dev_buf; free the handle with cm_desc_free and the buffer yourself.
+ * The descriptor is bound to one spec, batch shape and tile shape and is
+ * rebuilt from each batch's metadata (paper summary sections 3.1 and 3.3: the
+ * spec is compiled once, the descriptor is produced online per batch).
+ * CM_ERR_SIZE when bytes is too small, CM_ERR_INVALID when dev_buf is not
+ * 256-byte aligned. */
 cm_status cm_desc_init(const cm_spec* spec, int32_t B, int32_t N, int32_t seg_cap,
                        const cm_tiles* tiles, void* dev_buf, size_t bytes, cm_desc** out);
 void cm_desc_free(cm_desc* desc);
@@ -256,9 +264,11 @@ cm_status cm_spec_codegen(const cm_spec* spec, char* buf, size_t len, size_t* ne
 
 /* ---- online, every batch (section 3.3) --------------------------------- */
 
-/* One preprocess kernel launch: evaluate the compiled endpoints of `spec`
- * against `md` and write the whole descriptor (header, both interval tables,
- * both bitmaps, per-tile run maxima, error words).  desc must come from
+/* One preprocess kernel launch (paper summary section 3.3 "Online Efficient
+ * Mask Attention Execution", with the descriptor contents of section 3.3.1):
+ * evaluate the compiled endpoints of `spec` against `md` and write the whole
+ * descriptor (header, both interval tables, both bitmaps, per-tile run
+ * maxima, error words).  desc must come from
  * cm_desc_init (md->cu_seqlens NULL) or cm_desc_init_packed (md->cu_seqlens
  * set) with the same spec.  Asynchronous on `stream`. */
 cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_desc* desc,
@@ -292,9 +302,14 @@ cm_status cm_build_descriptor(const cm_spec* spec, const cm_metadata* md, cm_des
 #define CM_PRED_RETRIEVAL 3
 cm_status cm_build_blockmask(int32_t family, const cm_metadata* md, cm_desc* desc, cm_stream stream);
 
-/* Forward: o (bf16) and lse (fp32, natural log; -inf for a row with no
- * visible key, whose o row is 0).  Requires d in {64, 128} and a descriptor
- * whose forward tiles are supported.  Asynchronous on `stream`. */
+/* Forward (paper summary section 3.3.2 "Descriptor-Guided Attention
+ * Execution": empty tiles skipped, full tiles unmasked, endpoint checks in
+ * partial tiles, invisible scores set to -inf before the online softmax):
+ * o (bf16) and lse (fp32, natural log; -inf for a row with no visible key,
+ * whose o row is 0).  q, k, v, o follow args' layout; every pointer is a
+ * caller-owned device pointer, 16-byte aligned.  Requires d in {64, 128} and
+ * a descriptor whose forward tiles are supported (CM_ERR_UNSUPPORTED), built
+ * for args' B and N (CM_ERR_MISMATCH).  Asynchronous on `stream`. */
 cm_status cm_attn_fwd(const cm_attn_args* args, const void* q, const void* k, const void* v,
                       const cm_desc* desc, void* o, float* lse, cm_stream stream);
 
@@ -302,10 +317,16 @@ cm_status cm_attn_fwd(const cm_attn_args* args, const void* q, const void* k, co
  * the row's lse in log2 units (2 * B * H * N floats). */
 cm_status cm_attn_bwd_workspace(const cm_attn_args* args, size_t* bytes);
 
-/* Backward from the forward's o and lse: dq, dk, dv (bf16).  Three kernels on
- * `stream`: D = rowsum(dO * O); dK/dV per key tile over the query tiles that
- * the backward bitmap marks non-empty (column runs in partial tiles); dQ per
- * query tile over the forward bitmap (row runs).  Deterministic (no atomics). */
+/* Backward from the forward's o and lse: dq, dk, dv (bf16).  Training
+ * throughput counts forward and backward (paper summary section 1), and the
+ * backward follows its own descriptor direction (section 3.3: per key column,
+ * with the backward spec's intervals).  Three kernels on `stream`: D =
+ * rowsum(dO * O); dK/dV per key tile over the query tiles that the backward
+ * bitmap marks non-empty (column runs in partial tiles); dQ per query tile
+ * over the forward bitmap (row runs).  Deterministic (no atomics).  The
+ * workspace (caller-owned device memory of cm_attn_bwd_workspace bytes, else
+ * CM_ERR_SIZE) holds D and the log2 lse between the kernels; same argument
+ * checks as cm_attn_fwd. */
 cm_status cm_attn_bwd(const cm_attn_args* args, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, const cm_desc* desc,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -336,6 +357,25 @@ cm_status cm_attn_bwd_stage(int32_t stage, const cm_attn_args* args, const void*
                             const void* v, const void* o, const float* lse, const void* dO,
                             const cm_desc* desc, void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, cm_stream stream);
+
+/* ---- test and debug (synchronising) ------------------------------------ */
+
+/* Copy the whole descriptor (cm_desc_offsets' total) into host memory:
+ * enqueued on `stream` after the work already there, then the stream is
+ * synchronised.  The descriptor of paper summary section 3.3.1, in the byte
+ * layout at the top of this header.  CM_ERR_SIZE when bytes is smaller than
+ * the descriptor; CM_ERR_HIP if the copy fails.  Not for the hot path. */
+cm_status cm_desc_download(const cm_desc* desc, void* host, size_t bytes, cm_stream stream);
+
+/* The metadata errors the preprocess found (paper summary section 3.1: the
+ * descriptor is built on the device from each batch's metadata, so errors
+ * there are found on the device): *flags = header word 13, the OR of the
+ * CM_MD_* bits of every sample (0 = valid metadata); with per_sample non-NULL
+ * also each sample's word (B words, or n_samples for a packed descriptor;
+ * n_per_sample gives that count when non-NULL).  Reads after the work already
+ * on `stream` and synchronises it.  Not for the hot path. */
+cm_status cm_desc_errors(const cm_desc* desc, uint32_t* flags, uint32_t* per_sample, int32_t* n_per_sample,
+                         cm_stream stream);
 
 /* ---- diagnostics -------------------------------------------------------- */
 const char* cm_status_str(cm_status status);

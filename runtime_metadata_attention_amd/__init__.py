@@ -33,7 +33,7 @@ EXPORTS = ("cm_spec_compile", "cm_spec_free", "cm_spec_info", "cm_spec_dump", "c
            "cm_desc_size", "cm_desc_init", "cm_desc_size_packed", "cm_desc_init_packed", "cm_desc_free",
            "cm_desc_offsets", "cm_build_descriptor", "cm_build_blockmask",
            "cm_attn_fwd", "cm_attn_bwd_workspace", "cm_attn_bwd", "cm_attn_bwd_stage",
-           "cm_attn_bwd_noalloc",
+           "cm_attn_bwd_noalloc", "cm_desc_download", "cm_desc_errors",
            "cm_status_str", "cm_last_error", "cm_version")
 
 
@@ -106,6 +106,8 @@ def library() -> ctypes.CDLL:
         "cm_attn_bwd": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "cm_attn_bwd_stage": (I32, [I32, P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "cm_attn_bwd_noalloc": (I32, [P(cm_attn_args), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]),
+        "cm_desc_download": (I32, [VP, VP, SZ, VP]),
+        "cm_desc_errors": (I32, [VP, P(ctypes.c_uint32), VP, P(I32), VP]),
         "cm_status_str": (ctypes.c_char_p, [I32]),
         "cm_last_error": (ctypes.c_char_p, []),
         "cm_version": (ctypes.c_char_p, []),
@@ -282,6 +284,25 @@ class Descriptor:
             self.handle = None
 
 
+def cm_desc_download(desc: Descriptor, stream=None):
+    """The whole descriptor as a host numpy uint32 array (synchronises)."""
+    import numpy as np
+
+    out = np.zeros(desc.bytes // 4, np.uint32)
+    _check(library().cm_desc_download(desc.handle, out.ctypes.data, out.nbytes, _stream(stream)), "cm_desc_download")
+    return out
+
+
+def cm_desc_errors(desc: Descriptor, stream=None):
+    """(OR of every sample's metadata-error bits, per-sample list); synchronises."""
+    n = desc.packed if desc.packed else desc.B
+    per = (ctypes.c_uint32 * max(1, n))()
+    flags, cnt = ctypes.c_uint32(), ctypes.c_int32()
+    _check(library().cm_desc_errors(desc.handle, ctypes.byref(flags), per, ctypes.byref(cnt), _stream(stream)),
+           "cm_desc_errors")
+    return flags.value, [per[i] for i in range(cnt.value)]
+
+
 def cm_desc_offsets(desc: Descriptor):
     out = (ctypes.c_size_t * 9)()
     _check(library().cm_desc_offsets(desc.handle, out), "cm_desc_offsets")
@@ -350,7 +371,47 @@ def _desc_handle(desc):
     return None if desc is None else desc.handle
 
 
+def _check_tensors(where: str, args: cm_attn_args, q, lse, **others):
+    """The C ABI applies args' shape and strides to every bf16 tensor: check
+    that q matches args and that each other tensor has q's shape, strides,
+    dtype and device, and lse is a contiguous fp32 [B, H, N] tensor there."""
+    import torch
+
+    def bad(msg):
+        raise ValueError(f"{where}: {msg}")
+
+    shape = (args.B, args.H, args.N, args.d)
+    if tuple(q.shape) != shape:
+        bad(f"q has shape {tuple(q.shape)}, args say {shape}")
+    if q.dtype != torch.bfloat16:
+        bad(f"q must be bfloat16, not {q.dtype}")
+    if (args.stride_b, args.stride_h, args.stride_n) != (0, 0, 0) and \
+            tuple(q.stride()[:3]) != (args.stride_b, args.stride_h, args.stride_n):
+        bad(f"q has strides {q.stride()}, args say {(args.stride_b, args.stride_h, args.stride_n, 1)}")
+    if q.stride()[3] != 1:
+        bad("the last dimension of q must be contiguous")
+    for name, t in others.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(q.shape):
+            bad(f"{name} has shape {tuple(t.shape)}, q has {tuple(q.shape)}")
+        if t.dtype != torch.bfloat16:
+            bad(f"{name} must be bfloat16, not {t.dtype}")
+        if t.stride() != q.stride():
+            bad(f"{name} has strides {t.stride()}, q has {q.stride()} (the kernels apply q's strides to every tensor)")
+        if t.device != q.device:
+            bad(f"{name} is on {t.device}, q on {q.device}")
+    if lse is not None:
+        if tuple(lse.shape) != shape[:3] or lse.dtype != torch.float32 or not lse.is_contiguous():
+            bad(f"lse must be a contiguous float32 tensor of shape {shape[:3]}, not {lse.dtype} {tuple(lse.shape)}")
+        if lse.device != q.device:
+            bad(f"lse is on {lse.device}, q on {q.device}")
+    if not q.is_cuda:
+        bad("tensors must be on the GPU")
+
+
 def cm_attn_fwd(args: cm_attn_args, q, k, v, desc, o, lse, stream=None):
+    _check_tensors("cm_attn_fwd", args, q, lse, k=k, v=v, o=o)
     _check(library().cm_attn_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _desc_handle(desc), _ptr(o),
                                  _ptr(lse), _stream(stream)), "cm_attn_fwd")
 
@@ -365,13 +426,24 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+def _check_workspace(where, args, workspace):
+    import torch
+
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError(f"{where}: the workspace must be a contiguous float32 tensor")
+
+
 def cm_attn_bwd(args: cm_attn_args, q, k, v, o, lse, do, desc, dq, dk, dv, workspace, stream=None):
+    _check_workspace("cm_attn_bwd", args, workspace)
+    _check_tensors("cm_attn_bwd", args, q, lse, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
     _check(library().cm_attn_bwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                  _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                  _nbytes(workspace), _stream(stream)), "cm_attn_bwd")
 
 
 def cm_attn_bwd_stage(stage: int, args: cm_attn_args, q, k, v, o, lse, do, desc, dq, dk, dv, workspace, stream=None):
+    _check_workspace("cm_attn_bwd_stage", args, workspace)
+    _check_tensors("cm_attn_bwd_stage", args, q, lse, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
     _check(library().cm_attn_bwd_stage(stage, ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        _ptr(do), _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                        _nbytes(workspace), _stream(stream)), "cm_attn_bwd_stage")
@@ -383,6 +455,7 @@ CM_NOALLOC_MAX_ROWS = 1 << 21
 def cm_attn_bwd_noalloc(args: cm_attn_args, q, k, v, o, lse, do, desc, dq, dk, dv, stream=None):
     """cm_attn_bwd with the library's fixed per-GPU workspace (no workspace
     argument; at most CM_NOALLOC_MAX_ROWS rows B * H * N per call)."""
+    _check_tensors("cm_attn_bwd_noalloc", args, q, lse, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv)
     _check(library().cm_attn_bwd_noalloc(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                          _desc_handle(desc), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
            "cm_attn_bwd_noalloc")

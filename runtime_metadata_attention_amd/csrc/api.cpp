@@ -463,6 +463,35 @@ cm_status cm_attn_bwd_noalloc(const cm_attn_args* args, const void* q, const voi
   return bwd_run(-1, args, q, k, v, o, lse, dO, desc, dq, dk, dv, nullptr, 0, true, stream);
 }
 
+cm_status cm_desc_download(const cm_desc* desc, void* host, size_t bytes, cm_stream stream) {
+  if (!desc || !host) return fail(CM_ERR_NULL, "desc and host are required");
+  const size_t total = desc->off[SEC_TOTAL];
+  if (bytes < total) return fail(CM_ERR_SIZE, "host buffer has " + std::to_string(bytes) + " bytes, the descriptor " +
+                                                  std::to_string(total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(host, desc->buf, total, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "cm_desc_download");
+  return CM_OK;
+}
+
+cm_status cm_desc_errors(const cm_desc* desc, uint32_t* flags, uint32_t* per_sample, int32_t* n_per_sample,
+                         cm_stream stream) {
+  if (!desc || !flags) return fail(CM_ERR_NULL, "desc and flags are required");
+  const int32_t n = desc->packed ? desc->packed : desc->B;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* base = static_cast<const uint8_t*>(desc->buf);
+  uint32_t header[16];
+  hipError_t e = hipMemcpyAsync(header, base, sizeof(header), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && per_sample)
+    e = hipMemcpyAsync(per_sample, base + desc->off[SEC_SAMPLE_ERR], size_t(n) * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "cm_desc_errors");
+  *flags = header[13];
+  if (n_per_sample) *n_per_sample = n;
+  return CM_OK;
+}
+
 const char* cm_status_str(cm_status status) {
   switch (status) {
     case CM_OK: return "ok";

@@ -10,7 +10,11 @@
  *   char  spec[spec_len]
  *   int32 scalars[B*n_scalars], seg_bounds[B*(seg_cap+1)], n_seg[B], refs[B*seg_cap*n_refs]
  *   bf16  q, k, v, dO: [B][H][N][d] each
- * Result file: bf16 o, dq, dk, dv; fp32 lse[B][H][N]; the descriptor bytes.
+ *   int32 has_bad; if 1, a second metadata set of the same sizes (scalars,
+ *         seg_bounds, n_seg, refs) that the device is to flag as invalid
+ * Result file: bf16 o, dq, dk, dv; fp32 lse[B][H][N]; the descriptor bytes;
+ * with has_bad also uint32 flags, uint32 per-sample error words[B] (from
+ * cm_desc_errors) and the second descriptor's bytes (from cm_desc_download).
  * Exit status 0 on success; otherwise the failing call is printed.
  */
 #include <stdio.h>
@@ -67,6 +71,13 @@ int main(int argc, char** argv) {
   const size_t elems = (size_t)B * H * N * d, tbytes = elems * 2, lbytes = (size_t)B * H * N * 4;
   unsigned char* inputs = (unsigned char*)malloc(4 * tbytes);
   if (read_all(f, inputs, 4 * tbytes)) return 2;
+  int32_t has_bad = 0;
+  int32_t* bad = NULL;
+  if (fread(&has_bad, 4, 1, f) != 1) has_bad = 0;
+  if (has_bad) {
+    bad = (int32_t*)malloc((n_sc + n_sb + B + n_rf + 1) * 4);
+    if (read_all(f, bad, (n_sc + n_sb + B + n_rf) * 4)) return 2;
+  }
   fclose(f);
 
   cm_spec* spec = NULL;
@@ -115,6 +126,33 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipMemcpy(out + 4 * tbytes + lbytes, dbuf, dbytes, hipMemcpyDeviceToHost));
   FILE* g = fopen(argv[2], "wb");
   if (!g || fwrite(out, 1, 4 * tbytes + lbytes + dbytes, g) != 4 * tbytes + lbytes + dbytes) return 3;
+
+  if (has_bad) {
+    /* the same descriptor rebuilt from metadata the device must reject */
+    cm_metadata bmd = md;
+    bmd.scalars = (const int32_t*)upload(bad, n_sc * 4);
+    bmd.seg_bounds = (const int32_t*)upload(bad + n_sc, n_sb * 4);
+    bmd.n_seg = (const int32_t*)upload(bad + n_sc + n_sb, (size_t)B * 4);
+    bmd.refs = (const int32_t*)upload(bad + n_sc + n_sb + B, n_rf * 4);
+    CHECK_CM(cm_build_descriptor(spec, &bmd, desc, NULL));
+    uint32_t flags = 0;
+    int32_t n_err = 0;
+    uint32_t* per = (uint32_t*)calloc((size_t)B, 4);
+    CHECK_CM(cm_desc_errors(desc, &flags, per, &n_err, NULL));
+    if (n_err != B) {
+      fprintf(stderr, "cm_desc_errors reported %d sample words, expected %d\n", n_err, B);
+      return 1;
+    }
+    unsigned char* words = (unsigned char*)malloc(dbytes);
+    if (cm_desc_download(desc, words, dbytes - 4, NULL) != CM_ERR_SIZE) {
+      fprintf(stderr, "cm_desc_download accepted a buffer smaller than the descriptor\n");
+      return 1;
+    }
+    CHECK_CM(cm_desc_download(desc, words, dbytes, NULL));
+    if (fwrite(&flags, 4, 1, g) != 1 || fwrite(per, 4, (size_t)B, g) != (size_t)B || fwrite(words, 1, dbytes, g) != dbytes)
+      return 3;
+    printf("c_driver: invalid metadata flagged 0x%x\n", flags);
+  }
   fclose(g);
 
   cm_desc_free(desc);

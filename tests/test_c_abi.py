@@ -17,6 +17,7 @@ import torch
 import runtime_metadata_attention_amd as cm
 from runtime_metadata_attention_amd import specs
 from oracle import descriptor as od
+from oracle import masks as om
 from tests.test_gpu_attention import run_gpu
 from tests.test_oracle_masks import small_md
 from workloads import make_tensors
@@ -48,6 +49,13 @@ def test_c_driver_matches_python_binding(tmp_path):
     B, H = 2, 2
     md = small_md(mask, N=N, seed=8, B=B)
     t = make_tensors(B, H, N, d, 81)
+    # metadata the device must flag: sample 0 claims more segments than the
+    # capacity, sample 1 starts its first segment past the sequence end
+    bad = md.copy()
+    bad.n_seg[0] = md.seg_cap + 1
+    bad.seg_bounds[1, 0] = N + 5
+    want_err = [om.validate(bad, b) for b in range(B)]
+    assert want_err[0] and want_err[1]
     text = specs.BY_MASK[mask].encode()
     job = tmp_path / "job.bin"
     with open(job, "wb") as f:
@@ -57,6 +65,9 @@ def test_c_driver_matches_python_binding(tmp_path):
             f.write(np.ascontiguousarray(a, dtype=np.int32).tobytes())
         for n in ("q", "k", "v", "do"):
             f.write(t[n].contiguous().view(torch.int16).numpy().tobytes())
+        f.write(struct.pack("<i", 1))
+        for a in (bad.scalars, bad.seg_bounds, bad.n_seg, bad.refs):
+            f.write(np.ascontiguousarray(a, dtype=np.int32).tobytes())
     exe = build_driver(str(tmp_path))
     res = tmp_path / "res.bin"
     print(f"[c-abi] {mask} B={B} H={H} N={N} d={d}", flush=True)
@@ -72,10 +83,19 @@ def test_c_driver_matches_python_binding(tmp_path):
         pos += 2 * n
     outs["lse"] = torch.from_numpy(np.frombuffer(raw, np.float32, B * H * N, pos).copy()).reshape(B, H, N)
     pos += 4 * B * H * N
-    words = np.frombuffer(raw, np.uint32, offset=pos)
-
     spec = cm.cm_spec_compile(specs.BY_MASK[mask])
     desc = cm.Descriptor(spec, B, N, md.seg_cap, tiles)
+    words = np.frombuffer(raw, np.uint32, desc.bytes // 4, pos)
+    pos += desc.bytes
+    flags = int(np.frombuffer(raw, np.uint32, 1, pos)[0])
+    per = np.frombuffer(raw, np.uint32, B, pos + 4).tolist()
+    bad_words = np.frombuffer(raw, np.uint32, desc.bytes // 4, pos + 4 + 4 * B)
+    # the invalid batch: its error words through cm_desc_errors, its whole
+    # descriptor through cm_desc_download, both against the oracle
+    assert per == want_err, (per, want_err)
+    assert flags == (want_err[0] | want_err[1])
+    assert np.array_equal(bad_words, od.build(mask, bad, desc.K_r, desc.K_c, tiles))
+
     assert words.nbytes == desc.bytes
     assert np.array_equal(words, od.build(mask, md, desc.K_r, desc.K_c, tiles))
     ref = run_gpu(specs.BY_MASK[mask], md, t, tiles, spec=spec, desc=desc)

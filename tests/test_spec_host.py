@@ -232,3 +232,39 @@ def test_specialised_source_embeds_the_program_and_compiles():
                             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                             "-I", csrc, "-c", f, "-o", os.path.join(d, "spec.o")], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_binding_rejects_tensors_that_do_not_match_q():
+    """The binding checks every tensor against q (shape, strides, dtype,
+    device) and lse's shape, dtype and layout before calling the library: the
+    C ABI applies q's strides to every tensor."""
+    import torch
+
+    B, H, N, d = 2, 3, 64, 128
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    args = cm.attn_args(q, causal=True)
+    good = dict(k=q.clone(), v=q.clone(), o=q.clone())
+    lse = torch.zeros(B, H, N)
+    cases = [
+        ("k", torch.zeros(B, H, N + 1, d, dtype=torch.bfloat16), "shape"),
+        ("v", torch.zeros(B, H, N, d, dtype=torch.float16), "bfloat16"),
+        ("o", torch.zeros(B, N, H, d, dtype=torch.bfloat16).transpose(1, 2), "strides"),
+    ]
+    for name, bad, what in cases:
+        kw = dict(good)
+        kw[name] = bad
+        with pytest.raises(ValueError, match=what):
+            cm.cm_attn_fwd(args, q, kw["k"], kw["v"], None, kw["o"], lse)
+    with pytest.raises(ValueError, match="lse"):
+        cm.cm_attn_fwd(args, q, good["k"], good["v"], None, good["o"], torch.zeros(B, H, N, dtype=torch.float64))
+    with pytest.raises(ValueError, match="lse"):
+        cm.cm_attn_fwd(args, q, good["k"], good["v"], None, good["o"], torch.zeros(B, N, H).transpose(1, 2))
+    with pytest.raises(ValueError, match="args"):
+        cm.cm_attn_fwd(cm.attn_args(q[:, :, :32]), q, good["k"], good["v"], None, good["o"], lse)
+    with pytest.raises(ValueError, match="GPU"):
+        cm.cm_attn_fwd(args, q, good["k"], good["v"], None, good["o"], lse)
+    ws = torch.zeros(16, dtype=torch.float64)
+    with pytest.raises(ValueError, match="workspace"):
+        cm.cm_attn_bwd(args, q, q, q, q, lse, q, None, q, q, q, ws)
+    with pytest.raises(ValueError, match="dq"):
+        cm.cm_attn_bwd(args, q, q, q, q, lse, q, None, q[:, :, :32], q, q, torch.zeros(16))
