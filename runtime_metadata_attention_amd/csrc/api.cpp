@@ -103,6 +103,7 @@ DescView desc_view(const cm_desc* d) {
   v.K_r = d->K_r; v.K_c = d->K_c; v.Wf = d->Wf; v.Wb = d->Wb;
   v.Tq_f = d->Tq_f; v.Tk_f = d->Tk_f; v.Tk_b = d->Tk_b; v.Tq_b = d->Tq_b;
   v.fq = d->tiles.fwd_q; v.fk = d->tiles.fwd_k; v.bk = d->tiles.bwd_k; v.bq = d->tiles.bwd_q;
+  v.packed = d->packed;
   std::memset(&v.pred, 0, sizeof(v.pred));
   v.pred.family = d->family;
   if (d->family >= 0) {

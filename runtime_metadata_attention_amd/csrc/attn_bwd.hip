@@ -719,6 +719,8 @@ hipError_t launch_bwd_dot(const AttnDims& a, const void* o, const void* dO, cons
 hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
                            const void* dO, const float* D, const DescView& dv, void* dk, void* dvv,
                            hipStream_t stream) {
+  // 128-key tiles with the default check and bf16 operands: 64 keys per wave
+  if (dkdv_wide_supported(a, dv)) return launch_bwd_dkdv_wide(a, q, k, v, dO, D, dv, dk, dvv, stream);
   BwdParams p = make_params(a, dv);
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);

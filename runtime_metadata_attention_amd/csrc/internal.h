@@ -96,6 +96,7 @@ struct DescView {                // device pointers into a descriptor
   const uint32_t* col_tkmax;
   int32_t K_r, K_c, Wf, Wb, Tq_f, Tk_f, Tk_b, Tq_b;
   int32_t fq, fk, bk, bq;
+  int32_t packed;                // packed batch: its sample count (0 for a padded batch or the causal path)
   PredView pred;
 };
 hipError_t launch_attn_fwd(const AttnDims& a, const void* q, const void* k, const void* v, const DescView& dv,
@@ -110,6 +111,11 @@ hipError_t launch_bwd_dkdv(const AttnDims& a, const void* q, const void* k, cons
 hipError_t launch_bwd_dq(const AttnDims& a, const void* q, const void* k, const void* v, const float* lse,
                          const void* dO, const float* D, const DescView& dv, void* dq, hipStream_t stream);
 bool attn_tiles_supported(int d, int fq, int fk, int bk, int bq);
+// dK/dV with 64 keys per wave (attn_dkdv_wide.hip): for 128-key backward
+// tiles of 64 query rows, the default check and bf16 operands
+bool dkdv_wide_supported(const AttnDims& a, const DescView& dv);
+hipError_t launch_bwd_dkdv_wide(const AttnDims& a, const void* q, const void* k, const void* v, const void* dO,
+                                const float* D, const DescView& dv, void* dk, void* dvv, hipStream_t stream);
 // The fixed backward workspace of cm_attn_bwd_noalloc: 2 * kScratchRows floats
 // per GPU; *ptr = its device address on the current device (looked up once
 // per device).

@@ -534,3 +534,21 @@ def test_causal_path_head_by_head_order():
         compare("dq", a["dq"][0, h], dq)
         compare("dk", a["dk"][0, h], dk)
         compare("dv", a["dv"][0, h], dv)
+
+
+WIDE_CASES = [
+    # mask, B, H, N, d, seed: N >= 8192 with one visible run per key column,
+    # where the dK/dV kernel with 64 keys per wave runs; N ragged and an odd
+    # number of 128-key tiles (the last work-group's second tile is empty)
+    ("shared_prompt", 1, 2, 8269, 128, 96),
+    ("causal", 1, 2, 8200, 64, 97),
+]
+
+
+@pytest.mark.parametrize("mask,B,H,N,d,seed", WIDE_CASES)
+def test_wide_dkdv_whole_tensor(mask, B, H, N, d, seed):
+    print(f"[attention-wide] {mask} B={B} H={H} N={N} d={d}", flush=True)
+    md = small_md(mask, N=N, seed=seed, B=B)
+    t = make_tensors(B, H, N, d, seed)
+    out = run_gpu(specs.BY_MASK[mask], md, t, (128, 64, 128, 64))
+    check_all(out, t, mask, md)
