@@ -144,11 +144,16 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     }
     if (wt.skip) continue;
 
-    // S^T = K Q^T for two 32-key blocks (operand reads pipelined ahead)
+    // S^T = K Q^T for two 32-key blocks (operand reads pipelined ahead).  The
+    // wave raises its priority while it issues matrix instructions, so that
+    // the SIMD's other wave does its softmax in the gaps rather than taking
+    // issue slots from the matrix stream.
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    __builtin_amdgcn_s_setprio(2);
     mfma_stream<D / 8, 4, 1>(
         [&](int i) { return lds_b128_at(cK + (i & 1) * (32 * D * 2) + lo.row[i >> 1]); },
         [&](int i, const bf16x8& a) { s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]); });
+    __builtin_amdgcn_s_setprio(0);
     if (wt.select) {
       if constexpr (PRED) mask_pred<true>(s, uint32_t(ct * BN + 4 * h), q, qvalid, ps, -INFINITY);
       else if constexpr (CHK == kCheckRunBits) apply_bits(s, wt.bits, -INFINITY);
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
 
     // O^T += V^T P^T (V read transposed from LDS; with the split precision
     // each V operand multiplies P's high and low bf16 parts)
+    __builtin_amdgcn_s_setprio(2);
     mfma_stream<4 * (D / 32), 4, 2, SPLIT ? 2 : 1>(
         [&](int i) {
           const int kc = i / (D / 32), db = i % (D / 32);
@@ -203,6 +209,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
           acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]);
           if constexpr (SPLIT) acc[i % (D / 32)] = mfma32(a, pl[i / (D / 32)], acc[i % (D / 32)]);
         });
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // epilogue: O = acc / l, lse = ln-sum-exp (natural log)
