@@ -138,7 +138,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
   const int wave = int(uniform(uint32_t(tid >> 6)));
   const int h = lane >> 5, lk = lane & 31;
   int pr, bh;
-  xcd_coords(int(blockIdx.x), p.pairs, p.B * p.H, p.pairs < kInterleaveBelow / 2, pr, bh);
+  // heads dealt tile by tile on each XCD: every head's longest key tiles
+  // (the first ones, seen by the most rows) start first (see
+  // dkdv_wide_supported)
+  xcd_coords(int(blockIdx.x), p.pairs, p.B * p.H, true, pr, bh);
   const int head = bh % p.H, b = bh / p.H;
   const int N = p.N;
   const int kt = 2 * pr + (wave >> 1);         // this wave's 128-key tile of the backward grid
@@ -462,20 +465,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
 
 // Work-group balance decides where the wide kernel pays.  A 256-key
 // work-group does the work of two 128-key ones, so the kernel ends later
-// when a few key tiles hold much more work than the rest:
-//  * masks whose key columns see several runs of rows (retrieval: the global
-//    prefix, seen by every row, holds up to eight times the mean work; a
-//    list-schedule model of retrieval4_32k puts the makespan 38% above the
-//    balanced one with 256-key work-groups, 1% with 128-key ones);
-//  * packed batches and short sequences, where each sample's history or
-//    prompt tiles are long and the rest short (measured: hstu_packed_64k
-//    8% slower, hstu_4k even).
-// So it takes single-run columns (K_c <= 1) of unpacked sequences of at
-// least 8192 tokens (causal_8k: dK/dV 8% faster, reward_model_32k 12% fewer
-// cycles); the rest keep the 32-keys-per-wave kernel.
+// when a few key tiles hold much more work than the rest and start late.
+// The kernel deals each XCD's heads tile by tile, so all of them start with
+// their first key tiles, which the most rows see: a list-schedule model puts
+// retrieval4_32k's makespan 1.8% above the balanced one (38% dealt head by
+// head: its global prefix, seen by every row, holds up to eight times the
+// mean work) and reward_model_32k's 0.9%.  Packed batches and short
+// sequences keep the 32-keys-per-wave kernel: there each sample's history or
+// prompt tiles dominate (hstu_4k: 18% above balanced with 256-key
+// work-groups against 0.2% with 128-key ones; hstu_packed_64k measured 8%
+// slower).
 bool dkdv_wide_supported(const AttnDims& a, const DescView& dv) {
   return (a.d == 128 || a.d == 64) && dv.bk == KT && dv.bq == BQ && a.check == CM_CHECK_RUN_BITS &&
-         a.precision == CM_PRECISION_BF16 && dv.K_c <= 1 && dv.packed == 0 && a.N >= 8192;
+         a.precision == CM_PRECISION_BF16 && dv.packed == 0 && a.N >= 8192;
 }
 
 hipError_t launch_bwd_dkdv_wide(const AttnDims& a, const void* q, const void* k, const void* v, const void* dO,
