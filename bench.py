@@ -57,12 +57,17 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 BF16_FLOP_PER_CLK = 256 * 4096  # MI355X: 256 CUs x 4096 dense bf16 flop per CU and cycle
 EXTRA_WORKLOADS = (("retrieval4_32k", False), ("causal_8k", False), ("causal_8k", True))
+# the step's kernels: their source files (for staleness of recorded counters)
+# and the prefix of their names in rocprofv3's output (the dK/dV stage runs
+# bwd_dkdv_kernel or bwd_dkdv_wide_kernel, by workload)
 KERNEL_SOURCES = {
-    "attn_fwd_kernel": "attn_fwd.hip",
-    "bwd_dkdv_kernel": "attn_bwd.hip",
-    "bwd_dq_kernel": "attn_bwd.hip",
-    "preprocess_kernel": "preprocess.hip",
+    "attn_fwd_kernel": ("attn_fwd.hip",),
+    "bwd_dkdv_kernel": ("attn_bwd.hip", "attn_dkdv_wide.hip"),
+    "bwd_dq_kernel": ("attn_bwd.hip",),
+    "preprocess_kernel": ("preprocess.hip", "preprocess_core.h"),
 }
+KERNEL_MATCH = {"attn_fwd_kernel": "attn_fwd_kernel", "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq_kernel",
+                "preprocess_kernel": "preprocess_kernel"}
 
 
 def log(*a):
@@ -70,10 +75,10 @@ def log(*a):
 
 
 def source_hash(kernel: str) -> str:
-    p = os.path.join(ROOT, "runtime_metadata_attention_amd", "csrc", KERNEL_SOURCES[kernel])
+    d = os.path.join(ROOT, "runtime_metadata_attention_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted({p, os.path.join(os.path.dirname(p), "attn_common.h")}):
-        h.update(open(f, "rb").read())
+    for f in sorted(set(KERNEL_SOURCES[kernel]) | {"attn_common.h"}):
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -123,7 +128,7 @@ def record_clock(csv_dir: str, workload: str = "reward_model_32k"):
     rec = json.load(open(path)) if os.path.exists(path) else {}
     lines = ["| kernel | dispatch | duration us | cycles (GRBM_GUI_ACTIVE / 8) | clock GHz |", "|---|---|---|---|---|"]
     for kernel in KERNEL_SOURCES:
-        rows = sorted((k[1], v) for k, v in per.items() if kernel in k[0])
+        rows = sorted((k[1], v) for k, v in per.items() if KERNEL_MATCH[kernel] in k[0])
         if not rows:
             continue
         clocks = []
@@ -204,7 +209,7 @@ def record_traffic(out_dir: str, workload: str = "reward_model_32k"):
              "| kernel | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | HBM bytes per launch (scaled) |",
              "|---|---|---|---|---|"]
     for kernel in KERNEL_SOURCES:
-        names = [n for n in kf if kernel in n]
+        names = [n for n in kf if KERNEL_MATCH[kernel] in n]
         if not names:
             continue
         fv = [x for n in names for x in kf[n]]
