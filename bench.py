@@ -45,6 +45,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -75,10 +76,15 @@ def log(*a):
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the kernel's sources with comments and blank space removed, so
+    that a counter record stays valid across edits of comments only."""
     d = os.path.join(ROOT, "runtime_metadata_attention_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(set(KERNEL_SOURCES[kernel]) | {"attn_common.h"}):
-        h.update(open(os.path.join(d, f), "rb").read())
+        text = open(os.path.join(d, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

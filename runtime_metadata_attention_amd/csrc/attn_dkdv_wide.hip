@@ -12,10 +12,10 @@
 // LDS feeds one matrix instruction, and at one wave per SIMD the LDS
 // instruction rate bounds the kernel.  Here a wave owns 64 keys (two 32-key
 // blocks), so each operand read feeds two matrix instructions, one per key
-// block: half the LDS reads per MFMA.  The price is registers: K and V of 64
-// keys as B operands (128 VGPRs) and the dK, dV accumulators (256 AGPRs: this
-// file is compiled without the VGPR-form MFMA option, so they stay in AGPRs
-// and only the score blocks live in VGPRs).
+// block: half the LDS reads per MFMA.  The price is registers: K of 64 keys
+// as a B operand (64 VGPRs) and the dK, dV accumulators (256 AGPRs, written
+// by the inline-asm accumulations below; the score blocks live in VGPRs).
+// V of the work-group's 256 keys stays in LDS and is read for dP.
 //
 // A work-group of four waves covers 256 keys: two consecutive key tiles of a
 // 128-key backward grid (waves 0-1 the first, 2-3 the second).  It walks the
