@@ -306,10 +306,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
       //   steps [NC, 2 NC)     dP += dO V^T   (dO rows)
       //   steps [T0, T0 + 2ND) dV^T += dO^T P (dO transposed), per 16-row chunk qc
       //   steps [T1, T1 + 2ND) dK^T += Q^T dS (Q transposed)
-      // Vector work rides along: the probabilities P = exp2(S log2e/sqrt(d) -
-      // lse2) in eight chunks from step NC + SK (late enough for the last S
-      // MFMAs to have finished), each chunk's bf16 operands just before its
-      // MFMAs, dS = P (dP - D) of chunk qc after its dV MFMAs.
+      // Vector work rides along, spread so that no step carries much more
+      // than its two MFMAs can hide:
+      //   the probabilities P = exp2(S log2e/sqrt(d) - lse2), eight chunks x
+      //     from step NC + SK (late enough for the last S MFMAs to finish);
+      //   chunk qc's bf16 P operands (masked in partial tiles), one key block
+      //     per step in the two steps before its dV MFMAs (after that step's
+      //     probabilities);
+      //   dS = P (dP - D) of chunk qc in ND parts from the last dV step of qc
+      //     (each chunk has its own P operands and D values, so chunk qc + 1
+      //     is prepared while chunk qc's MFMAs still read chunk qc's);
+      //   chunk qc's bf16 dS operands just before its dK MFMAs.
       constexpr int T0 = 2 * NC, T1 = T0 + 2 * ND, NOPS = T1 + 2 * ND, G = 3;
       constexpr int SK = NC / 4;  // exp chunks start this many steps after the last S MFMAs
       const char* qh = cur + hf * (32 * D * 2);
@@ -323,11 +330,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
       f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
       bf16x8 op[NOPS], vo[NOPS][2];
       auto rdv = [&](int i, int kb) { return lds_b128_at(sVw + kb * (32 * D * 2) + (rowx ^ (uint32_t(i - NC) << 5))); };
-      bf16x8 pb[2], sb[2];
+      bf16x8 pb[2][2], sb[2];  // pb[qc][kb]
       // lse2 of row group vg, read two steps before its first use (one
       // buffer per row group: with d = 64 the groups follow each other every
       // step); D of chunk qc's two row groups, read when its dV MFMAs start
-      float4 lbuf[4], dbuf[2];
+      float4 lbuf[4], dbuf[2][2];
       auto lse_step = [](int x) { return NC + SK + x * NC / 8; };  // the step of exp chunk x
 #pragma unroll
       for (int i = 0; i < G; ++i) {
@@ -336,28 +343,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
       }
 #pragma unroll
       for (int i = 0; i < NOPS; ++i) {
-        if (i >= T0 && i < T1 && (i - T0) % ND == 0) {
-          // P of chunk qc (elements 8 qc .. 8 qc + 7 of both key blocks),
-          // masked in partial tiles, to bf16
-          const int qc = (i - T0) / ND;
-          if (select) {
-            const uint32_t sh = 16 * hf + 8 * qc;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const uint32_t bits = (kb ? bits1 : bits0) >> sh;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t m = uint32_t(int32_t(bits << (31 - e)) >> 31);
-                const float sv = s[kb][8 * qc + e];
-                s[kb][8 * qc + e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sv) & m);
-              }
-            }
-          }
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kb][e] = (__bf16)s[kb][8 * qc + e];
-        }
         if (i >= T1 && (i - T1) % ND == 0) {
           const int qc = (i - T1) / ND;
 #pragma unroll
@@ -374,8 +359,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
           if (i == lse_step(2 * vg) - 2) lbuf[vg] = *reinterpret_cast<const float4*>(cL + hf * 32 + vg * 8 + 4 * h);
         if (i >= T0 && i < T1 && (i - T0) % ND == 0) {
           const int qc = (i - T0) / ND;
-          dbuf[0] = *reinterpret_cast<const float4*>(cD + hf * 32 + (2 * qc) * 8 + 4 * h);
-          dbuf[1] = *reinterpret_cast<const float4*>(cD + hf * 32 + (2 * qc + 1) * 8 + 4 * h);
+          dbuf[qc][0] = *reinterpret_cast<const float4*>(cD + hf * 32 + (2 * qc) * 8 + 4 * h);
+          dbuf[qc][1] = *reinterpret_cast<const float4*>(cD + hf * 32 + (2 * qc + 1) * 8 + 4 * h);
         }
         if (i < NC) {
           s[0] = mfma32(op[i], kreg[0][i], s[0]);
@@ -384,10 +369,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
           dp[0] = mfma32(op[i], vo[i][0], dp[0]);
           dp[1] = mfma32(op[i], vo[i][1], dp[1]);
         } else if (i < T1) {
-          const int db = (i - T0) % ND;
-          if (db == 0) mfma_acc<true>(adv[db][0], op[i], pb[0]);
-          else mfma_acc<false>(adv[db][0], op[i], pb[0]);
-          mfma_acc<false>(adv[db][1], op[i], pb[1]);
+          const int qc = (i - T0) / ND, db = (i - T0) % ND;
+          if (db == 0) mfma_acc<true>(adv[db][0], op[i], pb[qc][0]);
+          else mfma_acc<false>(adv[db][0], op[i], pb[qc][0]);
+          mfma_acc<false>(adv[db][1], op[i], pb[qc][1]);
         } else {
           const int db = (i - T1) % ND;
           if (db == 0) mfma_acc<true>(adk[db][0], op[i], sb[0]);
@@ -404,24 +389,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             s[kb][4 * vg + e] = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * vg + e], p.scale_log2, -lv[e]));
+          // (pins the chunk to this step: instruction selection would
+          // otherwise sink it to its first use and pile chunks up there)
+          asm volatile("" : "+v"(s[kb]));
         }
-        if (i >= T0 && i < T1 && (i - T0) % ND == ND - 1) {
-          // dS of the chunk just used for dV: row groups 2 qc and 2 qc + 1
-          const int qc = (i - T0) / ND;
+        // the bf16 P operands of chunk qc, key block kb (elements 8 qc ..
+        // 8 qc + 7), masked in partial tiles
 #pragma unroll
-          for (int g = 0; g < 2; ++g) {
+        for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if (i != T0 + qc * ND - 2 + kb) continue;
+            if (select) {
+              const uint32_t bits = (kb ? bits1 : bits0) >> (16 * hf + 8 * qc);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t m = uint32_t(int32_t(bits << (31 - e)) >> 31);
+                const float sv = s[kb][8 * qc + e];
+                s[kb][8 * qc + e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sv) & m);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[qc][kb][e] = (__bf16)s[kb][8 * qc + e];
+            asm volatile("" : "+v"(pb[qc][kb]), "+v"(s[kb]));
+          }
+        // dS of chunk qc in ND parts (row group 2 qc + part / (ND / 2)), from
+        // its last dV step
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+          for (int part = 0; part < ND; ++part) {
+            if (i != T0 + qc * ND + ND - 1 + part) continue;
+            constexpr int PER = 16 / ND;  // elements per part (of 2 row groups x 2 key blocks x 4)
+            const int g = (part * PER) / 8, kb = ((part * PER) / 4) & 1, e0 = (part * PER) % 4;
             const int vg = 2 * qc + g;
-            const float4 d4 = dbuf[g];
+            const float4 d4 = dbuf[qc][g];
             const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int v = 4 * vg + e;
-                dp[kb][v] = s[kb][v] * (dp[kb][v] - dv4[e]);
-              }
+            for (int k = 0; k < PER; ++k) {
+              const int kk = (e0 + k) / 4, e = (e0 + k) % 4;  // (for PER = 8: both key blocks)
+              const int kbx = (kb + kk) & 1;
+              const int v = 4 * vg + e;
+              dp[kbx][v] = s[kbx][v] * (dp[kbx][v] - dv4[e]);
+            }
+            asm volatile("" : "+v"(dp[0]), "+v"(dp[1]));
           }
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
