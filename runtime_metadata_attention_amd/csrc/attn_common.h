@@ -60,6 +60,17 @@ __device__ __forceinline__ bf16x8 cat4(const bf16x4& a, const bf16x4& b) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x, x of lane l ^ 32) without a trip through LDS: gfx950's
+// v_permlane32_swap exchanges the upper 32 lanes of one register with the
+// lower 32 of another, so swapping two copies of x leaves x's lower half in
+// both halves of one and its upper half in both halves of the other.  (The
+// wait states cover a vector write of the copies just before.)
+__device__ __forceinline__ float wave_xor32_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Swizzled row-major LDS tile of D bf16 columns (no padding).  The 16-byte

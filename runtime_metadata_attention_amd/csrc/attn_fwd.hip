@@ -169,7 +169,7 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
-    mt = fmaxf(mt, wave_xor32(mt)) * p.scale_log2;
+    mt = wave_xor32_max(mt) * p.scale_log2;
     if (__any(mt > m + 8.f)) {
       const float mn = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.f : mn));
