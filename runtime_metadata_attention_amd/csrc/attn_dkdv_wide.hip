@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
       //     (each chunk has its own P operands and D values, so chunk qc + 1
       //     is prepared while chunk qc's MFMAs still read chunk qc's);
       //   chunk qc's bf16 dS operands just before its dK MFMAs.
-      constexpr int T0 = 2 * NC, T1 = T0 + 2 * ND, NOPS = T1 + 2 * ND, G = 3;
+      constexpr int T0 = 2 * NC, T1 = T0 + 2 * ND, NOPS = T1 + 2 * ND, G = 4;
       constexpr int SK = NC / 4;  // exp chunks start this many steps after the last S MFMAs
       const char* qh = cur + hf * (32 * D * 2);
       auto rd = [&](int i) -> bf16x8 {
