@@ -661,18 +661,22 @@ __device__ __forceinline__ void xcd_coords(int w, int tiles, int hb, bool interl
 }
 
 // Visit the non-empty tiles of one bitmap row (codes 1 full, 2 partial).
+// The next bitmap word is loaded while the current one is consumed, so the
+// wave does not wait for a memory round trip every 16 tiles.
 struct TileIter {
   const uint32_t* words;
   int W, w;
-  uint32_t word, pending;
+  uint32_t word, pending, ahead;
   __device__ void init(const uint32_t* p, int nwords) {
     words = p; W = nwords; w = -1; word = 0; pending = 0;
+    ahead = nwords > 0 ? p[0] : 0u;
   }
   // next non-empty tile; false at the end
   __device__ __forceinline__ bool next(int& tile, int& state) {
     while (pending == 0) {
       if (++w >= W) return false;
-      word = uniform(words[w]);
+      word = uniform(ahead);
+      if (w + 1 < W) ahead = words[w + 1];
       pending = (word | (word >> 1)) & 0x55555555u;
     }
     const int bit = __builtin_ctz(pending);

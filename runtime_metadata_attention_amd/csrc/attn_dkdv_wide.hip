@@ -245,6 +245,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
   const int Tq = (N + BQ - 1) / BQ;
   int w = -1, cnext = (pr * 256) / BQ;
   uint32_t word0 = 0, word1 = 0, pending = 0;
+  // the next bitmap words, loaded while the current ones are consumed
+  uint32_t ahead0 = 0, ahead1 = 0;
+  if (!CAUSAL && p.Wb > 0) {
+    ahead0 = row0[0];
+    ahead1 = has1 ? row1[0] : 0u;
+  }
   auto next_tile = [&](int& tile, int& state) -> bool {
     if (CAUSAL) {
       if (cnext >= Tq) return false;
@@ -256,8 +262,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
     }
     while (pending == 0) {
       if (++w >= p.Wb) return false;
-      word0 = uniform(row0[w]);
-      word1 = has1 ? uniform(row1[w]) : 0u;
+      word0 = uniform(ahead0);
+      word1 = uniform(ahead1);
+      if (w + 1 < p.Wb) {
+        ahead0 = row0[w + 1];
+        ahead1 = has1 ? row1[w + 1] : 0u;
+      }
       pending = ((word0 | (word0 >> 1)) | (word1 | (word1 >> 1))) & 0x55555555u;
     }
     const int bit = __builtin_ctz(pending);
