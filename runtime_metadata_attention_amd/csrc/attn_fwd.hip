@@ -184,31 +184,56 @@ __global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
     float rsum = 0.f;
     constexpr bool SPLIT = PREC == kPrecSplit;
     bf16x8 pb[4], pl[SPLIT ? 4 : 1];
+    // probabilities of elements [4 g, 4 g + 4) of key chunk kc (16 keys)
+    auto probs = [&](int kc, int g) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 4 * g; e < 4 * g + 4; ++e) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][(kc & 1) * 8 + e], p.scale_log2, -mu));
         rsum += pe;
         pb[kc][e] = (__bf16)pe;
         if constexpr (SPLIT) pl[kc][e] = bf16_lo(pe, pb[kc][e]);
       }
+    };
+    // key block 0 (chunks 0 and 1) now; key block 1 beside the PV MFMAs of
+    // block 0, which do not need it
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      probs(kc, 0);
+      probs(kc, 1);
     }
-    lsum += rsum;
 
     // O^T += V^T P^T (V read transposed from LDS; with the split precision
-    // each V operand multiplies P's high and low bf16 parts)
+    // each V operand multiplies P's high and low bf16 parts), in fenced steps
+    // of one MFMA (two with the split precision); the operand reads run four
+    // steps ahead, and steps 0, 2, 4, 6 of block 0 form a quarter of block 1's
+    // probabilities each (pinned to their step)
     __builtin_amdgcn_s_setprio(2);
-    mfma_stream<4 * (D / 32), 4, 2, SPLIT ? 2 : 1>(
-        [&](int i) {
-          const int kc = i / (D / 32), db = i % (D / 32);
-          const char* t = cV + kc * (16 * D * 2);
-          return lds_tr8_at(t + lo.tr(db, 0), t + lo.tr(db, 1));
-        },
-        [&](int i, const bf16x8& a) {
-          acc[i % (D / 32)] = mfma32(a, pb[i / (D / 32)], acc[i % (D / 32)]);
-          if constexpr (SPLIT) acc[i % (D / 32)] = mfma32(a, pl[i / (D / 32)], acc[i % (D / 32)]);
-        });
+    {
+      constexpr int NM = 4 * (D / 32), G = 4, NB0 = 2 * (D / 32);
+      auto rd = [&](int i) {
+        const int kc = i / (D / 32), db = i % (D / 32);
+        const char* t = cV + kc * (16 * D * 2);
+        return lds_tr8_at(t + lo.tr(db, 0), t + lo.tr(db, 1));
+      };
+      bf16x8 op[NM];
+#pragma unroll
+      for (int i = 0; i < G; ++i) op[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        if (i + G < NM) op[i + G] = rd(i + G);
+        acc[i % (D / 32)] = mfma32(op[i], pb[i / (D / 32)], acc[i % (D / 32)]);
+        if constexpr (SPLIT) acc[i % (D / 32)] = mfma32(op[i], pl[i / (D / 32)], acc[i % (D / 32)]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (i != x * NB0 / 4) continue;
+          probs(2 + (x >> 1), x & 1);
+          asm volatile("" : "+v"(pb[2 + (x >> 1)]), "+v"(rsum));
+          if constexpr (SPLIT) asm volatile("" : "+v"(pl[2 + (x >> 1)]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    lsum += rsum;
     __builtin_amdgcn_s_setprio(0);
   }
 
