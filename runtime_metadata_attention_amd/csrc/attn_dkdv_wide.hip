@@ -360,6 +360,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sb[kb][e] = (__bf16)dp[kb][8 * qc + e];
         }
+        // the step's MFMA for key block kb
+        auto mma_kb = [&](int kb) {
+          if (i < NC) {
+            s[kb] = mfma32(op[i], kreg[kb][i], s[kb]);
+          } else if (i < T0) {
+            dp[kb] = mfma32(op[i], vo[i][kb], dp[kb]);
+          } else if (i < T1) {
+            const int qc = (i - T0) / ND, db = (i - T0) % ND;
+            if (db == 0 && kb == 0) mfma_acc<true>(adv[db][kb], op[i], pb[qc][kb]);
+            else mfma_acc<false>(adv[db][kb], op[i], pb[qc][kb]);
+          } else {
+            const int db = (i - T1) % ND;
+            if (db == 0 && kb == 0) mfma_acc<true>(adk[db][kb], op[i], sb[kb]);
+            else mfma_acc<false>(adk[db][kb], op[i], sb[kb]);
+          }
+        };
+        // The vector work sits between and after the step's two MFMAs, so
+        // that it issues in the shadow of each of them rather than in that of
+        // the second only.
+        mma_kb(0);
+        __builtin_amdgcn_sched_barrier(0);
         if (i + G < NOPS) {
           op[i + G] = rd(i + G);
           if (i + G >= NC && i + G < T0) { vo[i + G][0] = rdv(i + G, 0); vo[i + G][1] = rdv(i + G, 1); }
@@ -371,23 +392,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
           const int qc = (i - T0) / ND;
           dbuf[qc][0] = *reinterpret_cast<const float4*>(cD + hf * 32 + (2 * qc) * 8 + 4 * h);
           dbuf[qc][1] = *reinterpret_cast<const float4*>(cD + hf * 32 + (2 * qc + 1) * 8 + 4 * h);
-        }
-        if (i < NC) {
-          s[0] = mfma32(op[i], kreg[0][i], s[0]);
-          s[1] = mfma32(op[i], kreg[1][i], s[1]);
-        } else if (i < T0) {
-          dp[0] = mfma32(op[i], vo[i][0], dp[0]);
-          dp[1] = mfma32(op[i], vo[i][1], dp[1]);
-        } else if (i < T1) {
-          const int qc = (i - T0) / ND, db = (i - T0) % ND;
-          if (db == 0) mfma_acc<true>(adv[db][0], op[i], pb[qc][0]);
-          else mfma_acc<false>(adv[db][0], op[i], pb[qc][0]);
-          mfma_acc<false>(adv[db][1], op[i], pb[qc][1]);
-        } else {
-          const int db = (i - T1) % ND;
-          if (db == 0) mfma_acc<true>(adk[db][0], op[i], sb[0]);
-          else mfma_acc<false>(adk[db][0], op[i], sb[0]);
-          mfma_acc<false>(adk[db][1], op[i], sb[1]);
         }
         // probability chunks x = 2 vg + kb (row group vg of the half, key block kb)
 #pragma unroll
@@ -403,6 +407,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
           // otherwise sink it to its first use and pile chunks up there)
           asm volatile("" : "+v"(s[kb]));
         }
+        mma_kb(1);
+        __builtin_amdgcn_sched_barrier(0);
         // the bf16 P operands of chunk qc, key block kb (elements 8 qc ..
         // 8 qc + 7), masked in partial tiles
 #pragma unroll
