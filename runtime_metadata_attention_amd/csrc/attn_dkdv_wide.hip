@@ -498,14 +498,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide_kernel(WideParams p) {
 // their first key tiles, which the most rows see: a list-schedule model puts
 // retrieval4_32k's makespan 1.8% above the balanced one (38% dealt head by
 // head: its global prefix, seen by every row, holds up to eight times the
-// mean work) and reward_model_32k's 0.9%.  Packed batches and short
-// sequences keep the 32-keys-per-wave kernel: there each sample's history or
-// prompt tiles dominate (hstu_4k: 18% above balanced with 256-key
-// work-groups against 0.2% with 128-key ones; hstu_packed_64k measured 8%
-// slower).
+// mean work) and reward_model_32k's 0.9%.  For hstu_4k (N 4096) the model
+// puts 256-key work-groups 18% above balanced against 0.2% with 128-key ones,
+// yet since the kernel's step schedule was tightened it runs 7% faster there
+// all the same (same-box A/B).  Packed batches keep the 32-keys-per-wave
+// kernel (hstu_packed_64k: 2% slower with this one), and so do short
+// sequences, where a head has only a few work-groups.
 bool dkdv_wide_supported(const AttnDims& a, const DescView& dv) {
   return (a.d == 128 || a.d == 64) && dv.bk == KT && dv.bq == BQ && a.check == CM_CHECK_RUN_BITS &&
-         a.precision == CM_PRECISION_BF16 && dv.packed == 0 && a.N >= 8192;
+         a.precision == CM_PRECISION_BF16 && dv.packed == 0 && a.N >= 2048;
 }
 
 hipError_t launch_bwd_dkdv_wide(const AttnDims& a, const void* q, const void* k, const void* v, const void* dO,

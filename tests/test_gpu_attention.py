@@ -537,11 +537,14 @@ def test_causal_path_head_by_head_order():
 
 
 WIDE_CASES = [
-    # mask, B, H, N, d, seed: N >= 8192 with one visible run per key column,
-    # where the dK/dV kernel with 64 keys per wave runs; N ragged and an odd
-    # number of 128-key tiles (the last work-group's second tile is empty)
+    # mask, B, H, N, d, seed: unpacked batches with N >= 2048, where the dK/dV
+    # kernel with 64 keys per wave runs; N ragged and an odd number of 128-key
+    # tiles (the last work-group's second tile is empty); B * H = 8 engages
+    # the XCD order; retrieval gives key columns several visible-row runs
     ("shared_prompt", 1, 2, 8269, 128, 96),
     ("causal", 1, 2, 8200, 64, 97),
+    ("hstu", 2, 4, 2100, 128, 98),
+    ("retrieval", 1, 2, 3000, 64, 99),
 ]
 
 
