@@ -394,7 +394,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(BwdParams p) {
 // ------------------------------------------------------------------ dQ
 
 template <int D, int BM, bool CAUSAL, int CHK, int PREC>
-__global__ __launch_bounds__(BM * 2, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BM * 2, BM == 128 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
   constexpr bool SPLIT = PREC == kPrecSplit;  // dS as hi + lo bf16 operand pairs
   constexpr int NW = BM / 32;
   constexpr int TILE = BN * D;

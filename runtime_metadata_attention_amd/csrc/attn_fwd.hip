@@ -47,7 +47,7 @@ constexpr int BN = 64;
 constexpr int MAXR = 4;  // runs kept in registers; more are read from memory
 
 template <int D, int BM, bool CAUSAL, int CHK, int PREC>
-__global__ __launch_bounds__(BM * 2, 2) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(BM * 2, BM == 128 ? 2 : 1) void attn_fwd_kernel(FwdParams p) {
   constexpr int NW = BM / 32;
   // K and V tiles, double-buffered, swizzled (see swz())
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
