@@ -15,9 +15,12 @@ default workload (reward_model_32k) the line carries `by_workload`: the other
 descriptor and through the maskless causal path, and their ratio), measured
 the same way in the same run.
 
-Step times come from HIP events around every kernel of every timed step;
-`ms_per_step` is the wall clock over the timed steps, `step_ms` the median
-and 10th/90th percentiles of the per-step event times.
+The timed steps call the backward as one `cm_attn_bwd`, as a caller does
+(on short grids the library runs dQ beside dK/dV on a second stream);
+`ms_per_step` is the wall clock over them, `step_ms` the median and
+10th/90th percentiles of HIP events around each step.  A second pass of the
+same number of steps calls the three backward kernels one by one, with HIP
+events around every kernel: `kernel_ms` and the roofline come from it.
 
 HBM traffic of the dominant kernel comes from rocprofv3 counter runs:
 
@@ -513,7 +516,7 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
 
     names = ["preprocess_kernel", "attn_fwd_kernel", "bwd_dot_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
 
-    def step(events=None):
+    def step(events=None, staged=False):
         def mark(i):
             if events is not None:
                 events[i].record()
@@ -525,9 +528,13 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         mark(1)
         cm.cm_attn_fwd(args, q, k, v, use_desc, o, lse)
         mark(2)
-        for s in range(3):
-            cm.cm_attn_bwd_stage(s, args, q, k, v, o, lse, do, use_desc, dq, dk, dv, ws)
-            mark(3 + s)
+        if staged:
+            for s in range(3):
+                cm.cm_attn_bwd_stage(s, args, q, k, v, o, lse, do, use_desc, dq, dk, dv, ws)
+                mark(3 + s)
+        else:
+            cm.cm_attn_bwd(args, q, k, v, o, lse, do, use_desc, dq, dk, dv, ws)
+            mark(3)
 
     cm.cm_build_descriptor(spec, dmd, desc)  # (also counts V for the causal comparator)
     torch.cuda.synchronize()
@@ -536,20 +543,25 @@ def measure(workload: str, causal_path: bool, steps: int, warmup: int, cpu: bool
         step()
     torch.cuda.synchronize()
     log(f"warmup done; visible pairs V = {V}")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / steps
+    step_ev = np.array([e[0].elapsed_time(e[3]) for e in evs])  # ms, first to last event of each step
+    # per-kernel times: the same number of steps again, the backward's kernels called one by one
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for i in range(steps):
+        step(sevs[i], staged=True)
+    torch.cuda.synchronize()
     per = np.zeros((steps, 5))
-    for i, e in enumerate(evs):
+    for i, e in enumerate(sevs):
         for j in range(5):
             per[i, j] = e[j].elapsed_time(e[j + 1])  # ms
     avg = per.mean(axis=0)
-    ms_step = wall * 1e3 / steps
-    step_ev = np.array([e[0].elapsed_time(e[5]) for e in evs])  # ms, first to last event of each step
     step_ms = {"median": round(float(np.median(step_ev)), 4), "p10": round(float(np.percentile(step_ev, 10)), 4),
                "p90": round(float(np.percentile(step_ev, 90)), 4)}
     log("per-kernel ms: " + ", ".join(f"{n}={x:.4f}" for n, x in zip(names, avg)))

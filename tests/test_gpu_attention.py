@@ -342,6 +342,57 @@ def test_launches_follow_the_callers_stream():
         assert torch.equal(got.cpu(), ref[n]), n
 
 
+BESIDE_CASES = [
+    # B, H, N, seed: hstu_4k's shape (the dK/dV grid holds two work-groups per CU), smaller grids
+    (4, 8, 4096, 1003),
+    (2, 2, 1000, 41),
+    (1, 3, 700, 42),
+]
+
+
+@pytest.mark.parametrize("B,H,N,seed", BESIDE_CASES)
+def test_backward_with_dq_beside_dkdv_equals_the_kernels_one_by_one(B, H, N, seed):
+    """On short grids cm_attn_bwd runs dQ on a second stream beside dK/dV,
+    after D on the caller's stream, and the caller's stream waits for both.
+    The result equals the three backward kernels called one by one
+    (cm_attn_bwd_stage) bit for bit.  The call runs on a side stream whose
+    inputs are written only after a delay, and the outputs are copied on
+    that stream right after the call: a missing fork or join would read or
+    copy unfinished data."""
+    print(f"[attention-beside] hstu B={B} H={H} N={N} seed={seed}", flush=True)
+    if N == 4096:
+        md = make_metadata(WORKLOADS["hstu_4k"])
+    else:
+        md = small_md("hstu", N=N, seed=seed, B=B)
+    t = make_tensors(B, H, N, 128, seed)
+    tiles = (128, 64, 128, 64)
+    src = {n: t[n].cuda() for n in ("q", "k", "v", "do")}
+    spec = cm.cm_spec_compile(specs.HSTU)
+    desc = cm.Descriptor(spec, B, N, md.seg_cap, tiles)
+    cm.cm_build_descriptor(spec, cm.device_metadata(md), desc)
+    args = cm.attn_args(src["q"])
+    o = torch.empty_like(src["q"])
+    lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    cm.cm_attn_fwd(args, src["q"], src["k"], src["v"], desc, o, lse)
+    ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device="cuda")
+    ref = [torch.full_like(src["q"], float("nan")) for _ in range(3)]
+    for stage in range(3):
+        cm.cm_attn_bwd_stage(stage, args, src["q"], src["k"], src["v"], o, lse, src["do"], desc, *ref, ws)
+    torch.cuda.synchronize()
+    x = {n: torch.zeros_like(a) for n, a in src.items()}
+    got = [torch.full_like(src["q"], float("nan")) for _ in range(3)]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        _busy(100_000_000)
+        for n in x:
+            x[n].copy_(src[n])
+        cm.cm_attn_bwd(args, x["q"], x["k"], x["v"], o, lse, x["do"], desc, *got, ws)
+        copies = [g.clone() for g in got]
+    side.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), copies, ref):
+        assert torch.equal(a, b), name
+
+
 def test_step_captured_in_a_hip_graph_replays_with_new_metadata():
     """Descriptor build, forward and backward captured once into a HIP graph
     (the hot calls allocate, copy and clear nothing) and replayed with new
