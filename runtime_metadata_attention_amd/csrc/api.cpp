@@ -422,13 +422,21 @@ constexpr int kMaxSideDevices = 64;
 static std::mutex g_side_mu;
 static SideStream g_side[kMaxSideDevices];
 
-static hipError_t side_stream(SideStream** out) {
+// *out stays null (and the caller runs the backward on its own stream) when
+// the side stream does not exist yet and the caller's stream is being
+// captured: nothing is created inside a capture.
+static hipError_t side_stream(hipStream_t caller, SideStream** out) {
+  *out = nullptr;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
   SideStream& ss = g_side[dev];
   if (!ss.stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(caller, &cs);
+    if (e != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipSuccess;
     e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
@@ -480,11 +488,15 @@ static cm_status bwd_run(int32_t stage, const cm_attn_args* args, const void* q,
     e = scratch_workspace(&D);
     if (e != hipSuccess) return hip_fail(e, "cm_attn_bwd_noalloc (scratch address)");
   }
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  SideStream* ss = nullptr;
   if (stage == -1 && !fixed_scratch && overlap_backward(dims)) {
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* ss = nullptr;
-    e = side_stream(&ss);
-    if (e == hipSuccess) e = launch_bwd_dot(dims, o, dO, lse, D, s);
+    lock.lock();
+    e = side_stream(s, &ss);
+    if (e != hipSuccess) return hip_fail(e, "cm_attn_bwd (side stream)");
+  }
+  if (ss) {
+    e = launch_bwd_dot(dims, o, dO, lse, D, s);
     if (e == hipSuccess) e = hipEventRecord(ss->fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
     if (e == hipSuccess) e = launch_bwd_dkdv(dims, q, k, v, lse, dO, D, view, dk, dv, s);

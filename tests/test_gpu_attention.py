@@ -393,6 +393,63 @@ def test_backward_with_dq_beside_dkdv_equals_the_kernels_one_by_one(B, H, N, see
         assert torch.equal(a, b), name
 
 
+_FIRST_CALL_CAPTURED = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import runtime_metadata_attention_amd as cm
+from runtime_metadata_attention_amd import specs
+from tests.test_oracle_masks import small_md
+from workloads import make_tensors
+B, H, N = 2, 2, 1000
+md = small_md("hstu", N=N, seed=51, B=B)
+t = make_tensors(B, H, N, 128, 51)
+x = {n: t[n].cuda() for n in ("q", "k", "v", "do")}
+spec = cm.cm_spec_compile(specs.HSTU)
+desc = cm.Descriptor(spec, B, N, md.seg_cap, (128, 64, 128, 64))
+cm.cm_build_descriptor(spec, cm.device_metadata(md), desc)
+args = cm.attn_args(x["q"])
+o = torch.empty_like(x["q"])
+lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+cm.cm_attn_fwd(args, x["q"], x["k"], x["v"], desc, o, lse)
+ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device="cuda")
+got = [torch.full_like(o, float("nan")) for _ in range(3)]
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    cm.cm_attn_bwd(args, x["q"], x["k"], x["v"], o, lse, x["do"], desc, *got, ws)
+ref = [torch.full_like(o, float("nan")) for _ in range(3)]
+for stage in range(3):
+    cm.cm_attn_bwd_stage(stage, args, x["q"], x["k"], x["v"], o, lse, x["do"], desc, *ref, ws)
+for rep in range(3):
+    for a in got:
+        a.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), (rep, name)
+    print("replay", rep, "ok", flush=True)
+"""
+
+
+def test_first_backward_call_inside_a_graph_capture():
+    """A process whose first cm_attn_bwd call is captured into a HIP graph
+    (the library creates no stream inside a capture and runs that backward
+    on the caller's stream): every replay equals the kernels called one by
+    one.  Runs in a child process, so that no earlier call has set anything
+    up."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("[attention-capture-first] child process", flush=True)
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED, root], cwd=root, capture_output=True,
+                       text=True, timeout=100)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.count("ok") == 3
+
+
 def test_step_captured_in_a_hip_graph_replays_with_new_metadata():
     """Descriptor build, forward and backward captured once into a HIP graph
     (the hot calls allocate, copy and clear nothing) and replayed with new
