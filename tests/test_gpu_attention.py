@@ -393,6 +393,59 @@ def test_backward_with_dq_beside_dkdv_equals_the_kernels_one_by_one(B, H, N, see
         assert torch.equal(a, b), name
 
 
+def test_backward_from_two_host_threads_on_their_own_streams():
+    """Two host threads call cm_attn_bwd at the same time, each on its own
+    stream with its own tensors, on a grid short enough that the library runs
+    dQ on its side stream (shared by every caller on the device): each
+    thread's results equal the kernels called one by one, bit for bit."""
+    import threading
+
+    B, H, N = 2, 2, 1000
+    print(f"[attention-threads] hstu B={B} H={H} N={N}", flush=True)
+    cases = []
+    for seed in (61, 62):
+        md = small_md("hstu", N=N, seed=seed, B=B)
+        t = make_tensors(B, H, N, 128, seed)
+        x = {n: t[n].cuda() for n in ("q", "k", "v", "do")}
+        spec = cm.cm_spec_compile(specs.HSTU)
+        desc = cm.Descriptor(spec, B, N, md.seg_cap, (128, 64, 128, 64))
+        cm.cm_build_descriptor(spec, cm.device_metadata(md), desc)
+        args = cm.attn_args(x["q"])
+        o = torch.empty_like(x["q"])
+        lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+        cm.cm_attn_fwd(args, x["q"], x["k"], x["v"], desc, o, lse)
+        ws = torch.empty(cm.cm_attn_bwd_workspace(args) // 4, dtype=torch.float32, device="cuda")
+        ref = [torch.full_like(o, float("nan")) for _ in range(3)]
+        for stage in range(3):
+            cm.cm_attn_bwd_stage(stage, args, x["q"], x["k"], x["v"], o, lse, x["do"], desc, *ref, ws)
+        cases.append(dict(x=x, desc=desc, args=args, o=o, lse=lse, ref=ref,
+                          ws=torch.empty_like(ws), stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(c):
+        try:
+            with torch.cuda.stream(c["stream"]):
+                for _ in range(4):
+                    got = [torch.full_like(c["o"], float("nan")) for _ in range(3)]
+                    cm.cm_attn_bwd(c["args"], c["x"]["q"], c["x"]["k"], c["x"]["v"], c["o"], c["lse"], c["x"]["do"],
+                                   c["desc"], *got, c["ws"])
+                    c["stream"].synchronize()
+                    for name, a, b in zip(("dq", "dk", "dv"), got, c["ref"]):
+                        if not torch.equal(a, b):
+                            errors.append(name)
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(c,)) for c in cases]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=100)
+    assert not any(th.is_alive() for th in threads), "a thread did not finish"
+    assert not errors, errors
+
+
 _FIRST_CALL_CAPTURED = r"""
 import sys, torch
 sys.path.insert(0, sys.argv[1])
