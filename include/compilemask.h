@@ -27,6 +27,8 @@
  *   - Streams: `cm_stream` is a hipStream_t (NULL = the default stream).  The
  *     hot calls (cm_build_descriptor, cm_attn_fwd, cm_attn_bwd and
  *     cm_attn_bwd_stage) only enqueue kernels on it; they never synchronise.
+ *     (cm_attn_bwd on short grids also uses a library stream, forked from
+ *     and joined back to the caller's by events; see there.)
  *   - Errors: every call returns a cm_status.  A negative status means the
  *     call did nothing (no kernel launched, no output written); the detail is
  *     in cm_last_error() (thread-local, valid until the next call on the same
@@ -320,13 +322,17 @@ cm_status cm_attn_bwd_workspace(const cm_attn_args* args, size_t* bytes);
 /* Backward from the forward's o and lse: dq, dk, dv (bf16).  Training
  * throughput counts forward and backward (paper summary section 1), and the
  * backward follows its own descriptor direction (section 3.3: per key column,
- * with the backward spec's intervals).  Three kernels on `stream`: D =
- * rowsum(dO * O); dK/dV per key tile over the query tiles that the backward
- * bitmap marks non-empty (column runs in partial tiles); dQ per query tile
- * over the forward bitmap (row runs).  Deterministic (no atomics).  The
- * workspace (caller-owned device memory of cm_attn_bwd_workspace bytes, else
- * CM_ERR_SIZE) holds D and the log2 lse between the kernels; same argument
- * checks as cm_attn_fwd. */
+ * with the backward spec's intervals).  Three kernels: D = rowsum(dO * O);
+ * dK/dV per key tile over the query tiles that the backward bitmap marks
+ * non-empty (column runs in partial tiles); dQ per query tile over the
+ * forward bitmap (row runs).  Deterministic (no atomics).  All of it is
+ * ordered after earlier work on `stream` and before later work on it: when
+ * B * H * N <= 131072 the library runs dQ beside dK/dV on a stream of its
+ * own (one per device, created on the first such call outside a graph
+ * capture; a capture takes the fork and join along), with the same results.
+ * The workspace (caller-owned device memory of cm_attn_bwd_workspace bytes,
+ * else CM_ERR_SIZE) holds D and the log2 lse between the kernels; same
+ * argument checks as cm_attn_fwd. */
 cm_status cm_attn_bwd(const cm_attn_args* args, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, const cm_desc* desc,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -344,7 +350,7 @@ cm_status cm_attn_bwd(const cm_attn_args* args, const void* q, const void* k, co
  * on one stream are safe.  Every row the kernels read is written by the same
  * call first, so nothing needs clearing.  CM_ERR_SIZE when B * H * N exceeds
  * CM_NOALLOC_MAX_ROWS; otherwise the same arguments, checks, kernels and
- * results as cm_attn_bwd. */
+ * results as cm_attn_bwd, all three kernels on `stream` (no library stream). */
 #define CM_NOALLOC_MAX_ROWS (1 << 21)
 cm_status cm_attn_bwd_noalloc(const cm_attn_args* args, const void* q, const void* k, const void* v,
                               const void* o, const float* lse, const void* dO, const cm_desc* desc,
