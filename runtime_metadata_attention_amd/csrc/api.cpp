@@ -437,10 +437,16 @@ static hipError_t side_stream(hipStream_t caller, SideStream** out) {
     e = hipStreamIsCapturing(caller, &cs);
     if (e != hipSuccess) return e;
     if (cs != hipStreamCaptureStatusNone) return hipSuccess;
-    e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
+    SideStream made;
+    e = hipStreamCreateWithFlags(&made.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&made.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&made.join, hipEventDisableTiming);
+    if (e != hipSuccess) {  // keep nothing half made; a later call tries again
+      if (made.fork) (void)hipEventDestroy(made.fork);
+      if (made.stream) (void)hipStreamDestroy(made.stream);
+      return e;
+    }
+    ss = made;
   }
   *out = &ss;
   return hipSuccess;
